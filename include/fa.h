@@ -1,0 +1,117 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) causal attention forward library
+ * (libfa_mi355x.so).
+ *
+ * The operation is the forward pass described on the aiml.sh page "Speed up
+ * long contexts with FlashAttention" (lab.py, tiled_flash_attention; its
+ * dense reference is standard_attention): for every batch b, head h and query
+ * row i,
+ *
+ *     s_ij  = scale * (q_i . k_j)            for visible keys j
+ *     o_i   = sum_j softmax_j(s_ij) * v_j
+ *     lse_i = log(sum_j exp(s_ij))           (natural log, scale included)
+ *
+ * where key j is visible to row i when j <= i (causal) or always (non-causal).
+ * The result is computed tile by tile with an online softmax (running maximum,
+ * running sum, rescaled accumulator), so no S x S matrix ever reaches memory.
+ * The log-sum-exp output is not on the pages; it is what a caller needs to
+ * merge partial results over key shards or to run a backward pass.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major [B, H, S, D] (D fastest) for q, k, v, o and
+ *    [B, H, S] for lse.  Element type of q, k, v, o is `dtype`; lse is fp32.
+ *  - All pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates, frees and synchronises nothing; it enqueues work on `stream`
+ *    (a hipStream_t; NULL = the null stream) and returns after the enqueue.
+ *  - q, k, v, o must be 16-byte aligned, lse 4-byte aligned.  o must not
+ *    overlap q, k or v (not checked).  lse may be NULL (then not written).
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call enqueues nothing and returns a status, it never aborts.
+ *  - Non-finite inputs give undefined (but memory-safe) results.
+ *  - Calls on one stream are ordered; calls on different streams that write
+ *    the same o / lse race (the caller's responsibility).
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_dtype {
+  FA_DTYPE_FP32 = 0, /* IEEE binary32 */
+  FA_DTYPE_BF16 = 1  /* bfloat16 (1-8-7) */
+} fa_dtype;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* NULL / misaligned pointer, B, H, S or D < 1, non-finite scale */
+  FA_ERR_UNSUPPORTED = 2,      /* dtype, head dim, variant or size outside what is compiled */
+  FA_ERR_HIP = 3               /* the HIP runtime rejected the launch; see fa_last_hip_error() */
+} fa_status;
+
+/* Kernel variants.  FA_VARIANT_AUTO picks one from the shape; the others
+ * exist so tests can show that results do not depend on the tiling.
+ *   MFMA_Q64: bf16, D in {64, 128}; 256-query blocks, 4 waves x 64 queries.
+ *   MFMA_Q32: bf16, D in {64, 128}; 128-query blocks, 4 waves x 32 queries.
+ *   VALU:     fp32 or bf16, D in {16, 32, 64, 128}; one lane per query,
+ *             fp32 vector arithmetic (the fp32 path, and small head dims). */
+typedef enum fa_variant {
+  FA_VARIANT_AUTO = 0,
+  FA_VARIANT_MFMA_Q64 = 1,
+  FA_VARIANT_MFMA_Q32 = 2,
+  FA_VARIANT_VALU = 3
+} fa_variant;
+
+/*
+ * fa_fwd -- tiled online-softmax attention forward.
+ *
+ *   q, k, v   in : [B, H, S, D] dtype, device memory
+ *   o         out: [B, H, S, D] dtype, device memory
+ *   lse       out: [B, H, S] fp32, device memory, or NULL
+ *   B, H, S   batch, heads, sequence length (>= 1); any S (tails are masked)
+ *   D         head dim: 16, 32, 64 or 128 (bf16 64/128 run on the matrix cores)
+ *   causal    nonzero: key j visible to row i iff j <= i (the diagonal included)
+ *   scale     multiplies q.k; used as given (callers normally pass 1/sqrt(D))
+ *   dtype     FA_DTYPE_BF16 or FA_DTYPE_FP32; softmax state and accumulation
+ *             are fp32 either way, and bf16 probabilities feed the P.V product
+ *   stream    hipStream_t or NULL
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED (also when
+ * S*D >= 2^31 or the grid would exceed 2^31-1 blocks) or FA_ERR_HIP.
+ */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                 int64_t H, int64_t S, int64_t D, int causal, float scale, fa_dtype dtype,
+                 void *stream);
+
+/* fa_fwd with an explicit kernel variant (fa_variant); FA_ERR_UNSUPPORTED if
+ * that variant does not cover dtype/D.  Same arguments and semantics. */
+fa_status fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale,
+                         fa_dtype dtype, int variant, void *stream);
+
+/* The variant fa_fwd would run for this shape (an fa_variant value), or -1
+ * if the arguments are unsupported.  Host-only; touches no device. */
+int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype);
+
+/* Number of key/value tiles the causal tile scheduler of `variant` visits for
+ * one (batch, head) of length S (0 for an unsupported variant).  Host-only. */
+int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant);
+
+/* Static, never-NULL description of a status code. */
+const char *fa_status_str(fa_status status);
+
+/* hipError_t of the last FA_ERR_HIP returned on the calling thread (0 if none). */
+int fa_last_hip_error(void);
+
+/* Library version string, e.g. "fa_mi355x 0.1.0 gfx950". */
+const char *fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -20,6 +20,15 @@ _lib = None
 DTYPE_F32, DTYPE_BF16, DTYPE_F64 = 0, 1, 2
 
 
+def default_threads() -> int:
+    """Cores this process may run on, at most 16 (a GPU machine's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def library_path() -> str:
     return _LIB
 
@@ -91,7 +100,7 @@ def attention_dense(q, k, v, causal: bool = True, scale: float | None = None,
     lse = np.empty((n_bh, n_rows), dtype=np.float64)
     count = ctypes.c_int64(0)
     if n_threads is None:
-        n_threads = os.cpu_count() or 1
+        n_threads = default_threads()
     lib = _load()
     rc = lib.oracle_attention_dense(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, code, B, H, S, D, int(bool(causal)),

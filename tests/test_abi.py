@@ -1,0 +1,114 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and
+its host-side logic (argument checks, variant choice, tile scheduler counts) is
+right.  No call here reaches a kernel launch: every fa_fwd call below fails
+validation on the host, before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_online_softmax_causal_amd as fa
+from tiled_online_softmax_causal_amd.costmodel import causal_kv_tiles
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    declared = _declared_functions()
+    assert declared, "no declarations found in include/fa.h"
+    assert sorted(fa.EXPORTS) == declared
+    raw = ctypes.CDLL(fa.LIBRARY_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+    assert fa.version().startswith("fa_mi355x")
+    assert "gfx950" in fa.version()
+    assert lib.fa_last_hip_error() == 0
+
+
+def test_status_strings():
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARGUMENT, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, 99):
+        assert isinstance(fa.status_str(code), str) and fa.status_str(code)
+
+
+# Fake, 256-byte-aligned, never-dereferenced addresses: every call below is
+# rejected before the library touches them.
+P = 1 << 20
+
+
+@pytest.mark.parametrize("ptrs", [(0, P, P, P), (P, 0, P, P), (P, P, 0, P), (P, P, P, 0)])
+def test_null_pointer_rejected(ptrs):
+    assert fa.fa_fwd_raw(*ptrs, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("B,H,S,D", [(0, 1, 64, 128), (1, 0, 64, 128), (1, 1, 0, 128), (1, 1, 64, 0),
+                                     (-1, 1, 64, 128)])
+def test_bad_sizes_rejected(B, H, S, D):
+    assert fa.fa_fwd_raw(P, P, P, P, 0, B, H, S, D, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), -float("inf")])
+def test_non_finite_scale_rejected(scale):
+    assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, scale, fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_misaligned_pointers_rejected():
+    for i in range(4):
+        ptrs = [P, P, P, P]
+        ptrs[i] += 2
+        assert fa.fa_fwd_raw(*ptrs, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_fwd_raw(P, P, P, P, P + 2, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("D", [8, 48, 96, 256])
+def test_unsupported_head_dim(D):
+    assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, D, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_unsupported_dtype_and_variant():
+    assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, 7) == fa.FA_ERR_UNSUPPORTED
+    # the matrix-core variants are bf16-only and D in {64, 128}
+    assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_FP32,
+                         variant=fa.FA_VARIANT_MFMA_Q64) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 32, True, 0.1, fa.FA_DTYPE_BF16,
+                         variant=fa.FA_VARIANT_MFMA_Q32) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16, variant=42) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_size_limits_rejected():
+    # S * D must stay below 2^31 (32-bit offsets inside one head)
+    assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 1 << 24, 128, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_variant_selection():
+    bf16, f32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP32
+    assert fa.select_variant(8, 32, 8192, 128, bf16) == fa.FA_VARIANT_MFMA_Q64
+    assert fa.select_variant(1, 32, 1024, 128, bf16) == fa.FA_VARIANT_MFMA_Q32
+    assert fa.select_variant(1, 1, 64, 16, f32) == fa.FA_VARIANT_VALU
+    assert fa.select_variant(1, 1, 64, 16, bf16) == fa.FA_VARIANT_VALU
+    assert fa.select_variant(1, 1, 64, 128, f32) == fa.FA_VARIANT_VALU
+    assert fa.select_variant(1, 1, 64, 96, bf16) == -1
+    assert fa.select_variant(0, 1, 64, 128, bf16) == -1
+
+
+@pytest.mark.parametrize("S", [1, 2, 63, 64, 65, 255, 256, 257, 1000, 8192])
+@pytest.mark.parametrize("causal", [True, False])
+def test_scheduler_tile_counts(S, causal):
+    """The library's per-head tile count equals the causal block rule's closed form."""
+    for variant, bq, bk in ((fa.FA_VARIANT_MFMA_Q64, 256, 64), (fa.FA_VARIANT_MFMA_Q32, 128, 64),
+                            (fa.FA_VARIANT_VALU, 64, 32)):
+        assert fa.tiles_per_head(S, causal, variant) == causal_kv_tiles(S, bq, bk, causal)
+    assert fa.tiles_per_head(S, causal, 0) == 0
+
+
+def test_scheduler_page_worked_example():
+    """16x16 blocks over 64 rows visit 10 tiles (run-output.txt, flash_tiles_visited)."""
+    assert causal_kv_tiles(64, 16, 16) == 10

@@ -1,0 +1,156 @@
+"""MI355X (gfx950) tiled online-softmax attention forward.
+
+A thin ctypes binding over the C ABI of ``libfa_mi355x.so`` (declared in
+``include/fa.h``).  This module only marshals arguments: every step of the
+forward pass runs in the library's HIP kernels, and there is no fallback --
+if the library is missing or cannot be loaded, the first call raises.
+
+PyTorch supplies device memory and the current stream; nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG, "libfa_mi355x.so")
+
+FA_DTYPE_FP32, FA_DTYPE_BF16 = 0, 1
+FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_VARIANT_AUTO, FA_VARIANT_MFMA_Q64, FA_VARIANT_MFMA_Q32, FA_VARIANT_VALU = 0, 1, 2, 3
+VARIANTS = {"auto": 0, "mfma_q64": 1, "mfma_q32": 2, "valu": 3}
+
+# every symbol include/fa.h declares
+EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_fwd_select_variant", "fa_fwd_tiles_per_head",
+           "fa_status_str", "fa_last_hip_error", "fa_version")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: str = LIBRARY_PATH):
+    """Load libfa_mi355x.so and declare its C signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m tiled_online_softmax_causal_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, p]
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_variant.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, i32, p]
+    lib.fa_fwd_variant.restype = i32
+    lib.fa_fwd_select_variant.argtypes = [i64, i64, i64, i64, i32]
+    lib.fa_fwd_select_variant.restype = i32
+    lib.fa_fwd_tiles_per_head.argtypes = [i64, i32, i32]
+    lib.fa_fwd_tiles_per_head.restype = i64
+    lib.fa_status_str.argtypes = [i32]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_last_hip_error.restype = i32
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().fa_version().decode()
+
+
+def status_str(status: int) -> str:
+    return load_library().fa_status_str(status).decode()
+
+
+def select_variant(B: int, H: int, S: int, D: int, dtype: int = FA_DTYPE_BF16) -> int:
+    return load_library().fa_fwd_select_variant(B, H, S, D, dtype)
+
+
+def tiles_per_head(S: int, causal: bool, variant: int) -> int:
+    return load_library().fa_fwd_tiles_per_head(S, int(bool(causal)), variant)
+
+
+def kernel_name(variant: int, D: int, causal: bool) -> str:
+    """Name prefix of the kernel a variant launches (as profilers print it)."""
+    c = "true" if causal else "false"
+    if variant in (FA_VARIANT_MFMA_Q64, FA_VARIANT_MFMA_Q32):
+        return f"fa::attn_fwd_mfma_bf16<{D}, {2 if variant == FA_VARIANT_MFMA_Q64 else 1}, {c}>"
+    if variant == FA_VARIANT_VALU:
+        return "fa::attn_fwd_valu<"
+    raise ValueError(f"unknown variant {variant}")
+
+
+def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, S: int,
+               D: int, causal: bool, scale: float, dtype: int, stream: int = 0,
+               variant: int = FA_VARIANT_AUTO) -> int:
+    """Call fa_fwd_variant with raw device addresses; returns the fa_status code."""
+    lib = load_library()
+    return lib.fa_fwd_variant(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None,
+                              lse_ptr or None, B, H, S, D, int(bool(causal)), float(scale), dtype,
+                              int(variant), stream or None)
+
+
+def _check(status: int):
+    if status == FA_OK:
+        return
+    lib = load_library()
+    msg = lib.fa_status_str(status).decode()
+    if status == FA_ERR_HIP:
+        msg += f" (hipError_t {lib.fa_last_hip_error()})"
+    if status in (FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED):
+        raise ValueError(msg)
+    raise FAError(status, msg)
+
+
+def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
+        return_lse: bool = True, variant="auto", stream=None):
+    """Attention forward on ``[B, H, S, D]`` CUDA tensors (bf16 or fp32).
+
+    Returns ``(o, lse)`` -- ``o`` like ``q``, ``lse`` fp32 ``[B, H, S]`` (natural
+    log of the softmax denominator, scale included) -- or ``o`` alone when
+    ``return_lse`` is false.  ``scale`` defaults to ``1/sqrt(D)``.  The work is
+    enqueued on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    dtype = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_FP32}.get(q.dtype)
+    if dtype is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous device tensor like q")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H, S] tensor")
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        status = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr() if lse is not None else 0, B, H, S, D, causal, scale,
+                            dtype, st, variant)
+    _check(status)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,188 @@
+// C ABI of the attention forward library: argument checks, kernel choice,
+// causal tile scheduling and launch.  Declarations and the contract are in
+// include/fa.h.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_mfma_bf16.h"
+#include "fa_valu.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kNumXcd = 8;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t mfma_block_q(int variant) { return variant == FA_VARIANT_MFMA_Q64 ? 4 * 64 : 4 * 32; }
+
+bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
+  switch (variant) {
+    case FA_VARIANT_MFMA_Q64:
+    case FA_VARIANT_MFMA_Q32:
+      return dtype == FA_DTYPE_BF16 && (D == 64 || D == 128);
+    case FA_VARIANT_VALU:
+      return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP32) && (D == 16 || D == 32 || D == 64 || D == 128);
+    default:
+      return false;
+  }
+}
+
+// Shape-only choice: bf16 with D 64/128 runs on the matrix cores, 64 queries per
+// wave unless that leaves fewer than two workgroups per CU, where the 32-query
+// variant doubles the grid.
+int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
+  if (dtype == FA_DTYPE_BF16 && (D == 64 || D == 128)) {
+    const int64_t wgs = B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_Q64));
+    return wgs >= 2 * 256 ? FA_VARIANT_MFMA_Q64 : FA_VARIANT_MFMA_Q32;
+  }
+  if (variant_covers(FA_VARIANT_VALU, D, dtype)) return FA_VARIANT_VALU;
+  return -1;
+}
+
+template <int D, int NSUB>
+hipError_t launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                       int64_t S, int causal, float scale, hipStream_t stream) {
+  const int64_t bq = 4 * 32 * NSUB;
+  const int64_t n_qb = ceil_div(S, bq);
+  const int64_t grid = BH * n_qb;
+  const int xcd_group = (BH % kNumXcd) == 0;
+  const float c = std::fabs(scale) * kLog2e;
+  const int negate_q = scale < 0.f;
+  const auto* Q = static_cast<const uint16_t*>(q);
+  const auto* K = static_cast<const uint16_t*>(k);
+  const auto* V = static_cast<const uint16_t*>(v);
+  auto* O = static_cast<uint16_t*>(o);
+  if (causal)
+    hipLaunchKernelGGL((fa::attn_fwd_mfma_bf16<D, NSUB, true>), dim3((unsigned)grid), dim3(fa::kThreads), 0,
+                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)BH, c, negate_q, xcd_group);
+  else
+    hipLaunchKernelGGL((fa::attn_fwd_mfma_bf16<D, NSUB, false>), dim3((unsigned)grid), dim3(fa::kThreads), 0,
+                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)BH, c, negate_q, xcd_group);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_valu(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t S,
+                       int causal, float scale, hipStream_t stream) {
+  const int64_t n_qb = ceil_div(S, fa::kValuBQ);
+  const int64_t grid = BH * n_qb;
+  const float c = scale * kLog2e;
+  const auto* Q = static_cast<const T*>(q);
+  const auto* K = static_cast<const T*>(k);
+  const auto* V = static_cast<const T*>(v);
+  auto* O = static_cast<T*>(o);
+  if (causal)
+    hipLaunchKernelGGL((fa::attn_fwd_valu<T, D, true>), dim3((unsigned)grid), dim3(fa::kValuBQ), 0, stream, Q, K,
+                       V, O, lse, (int)S, (int)n_qb, c);
+  else
+    hipLaunchKernelGGL((fa::attn_fwd_valu<T, D, false>), dim3((unsigned)grid), dim3(fa::kValuBQ), 0, stream, Q, K,
+                       V, O, lse, (int)S, (int)n_qb, c);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_valu_d(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t S,
+                         int64_t D, int causal, float scale, hipStream_t stream) {
+  switch (D) {
+    case 16: return launch_valu<T, 16>(q, k, v, o, lse, BH, S, causal, scale, stream);
+    case 32: return launch_valu<T, 32>(q, k, v, o, lse, BH, S, causal, scale, stream);
+    case 64: return launch_valu<T, 64>(q, k, v, o, lse, BH, S, causal, scale, stream);
+    default: return launch_valu<T, 128>(q, k, v, o, lse, BH, S, causal, scale, stream);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
+  if (B < 1 || H < 1 || S < 1) return -1;
+  return select_variant(B, H, S, D, dtype);
+}
+
+int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant) {
+  int64_t bq, bk;
+  if (variant == FA_VARIANT_MFMA_Q64 || variant == FA_VARIANT_MFMA_Q32) {
+    bq = mfma_block_q(variant);
+    bk = fa::kBK;
+  } else if (variant == FA_VARIANT_VALU) {
+    bq = fa::kValuBQ;
+    bk = fa::kValuBK;
+  } else {
+    return 0;
+  }
+  if (S < 1) return 0;
+  int64_t tiles = 0;
+  for (int64_t q0 = 0; q0 < S; q0 += bq) {
+    const int64_t kv_end = causal ? (q0 + bq < S ? q0 + bq : S) : S;
+    tiles += ceil_div(kv_end, bk);
+  }
+  return tiles;
+}
+
+fa_status fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                         int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, int variant,
+                         void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARGUMENT;
+  if (B < 1 || H < 1 || S < 1 || D < 1) return FA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARGUMENT;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  // in-kernel offsets within one head are 32-bit; the grid is one dimension
+  if (S * D >= (int64_t(1) << 31) || B > INT32_MAX / H) return FA_ERR_UNSUPPORTED;
+  if (variant == FA_VARIANT_AUTO) variant = select_variant(B, H, S, D, dtype);
+  if (!variant_covers(variant, D, dtype)) return FA_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  const int64_t bq = variant == FA_VARIANT_VALU ? fa::kValuBQ : mfma_block_q(variant);
+  if (BH * ceil_div(S, bq) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (variant == FA_VARIANT_VALU) {
+    err = dtype == FA_DTYPE_FP32 ? launch_valu_d<float>(q, k, v, o, lse, BH, S, D, causal, scale, st)
+                                 : launch_valu_d<uint16_t>(q, k, v, o, lse, BH, S, D, causal, scale, st);
+  } else if (variant == FA_VARIANT_MFMA_Q64) {
+    err = D == 128 ? launch_mfma<128, 2>(q, k, v, o, lse, BH, S, causal, scale, st)
+                   : launch_mfma<64, 2>(q, k, v, o, lse, BH, S, causal, scale, st);
+  } else {
+    err = D == 128 ? launch_mfma<128, 1>(q, k, v, o, lse, BH, S, causal, scale, st)
+                   : launch_mfma<64, 1>(q, k, v, o, lse, BH, S, causal, scale, st);
+  }
+  if (err != hipSuccess) {
+    g_last_hip_error = static_cast<int>(err);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                 int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, void* stream) {
+  return fa_fwd_variant(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, FA_VARIANT_AUTO, stream);
+}
+
+const char* fa_status_str(fa_status status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype, head dim, variant or size";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+const char* fa_version(void) { return "fa_mi355x 0.1.0 gfx950"; }
+
+}  // extern "C"
