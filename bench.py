@@ -116,7 +116,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_q64", "mfma_q32", "valu"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_b256", "mfma_b128", "valu"])
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

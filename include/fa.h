@@ -55,14 +55,16 @@ typedef enum fa_status {
 
 /* Kernel variants.  FA_VARIANT_AUTO picks one from the shape; the others
  * exist so tests can show that results do not depend on the tiling.
- *   MFMA_Q64: bf16, D in {64, 128}; 256-query blocks, 4 waves x 64 queries.
- *   MFMA_Q32: bf16, D in {64, 128}; 128-query blocks, 4 waves x 32 queries.
- *   VALU:     fp32 or bf16, D in {16, 32, 64, 128}; one lane per query,
- *             fp32 vector arithmetic (the fp32 path, and small head dims). */
+ *   MFMA_B256: bf16, D in {64, 128}; 256-row query blocks, 8 waves of 32 rows in
+ *              two groups that alternate matrix-core and softmax phases.
+ *   MFMA_B128: bf16, D in {64, 128}; 128-row query blocks, 4 waves of 32 rows,
+ *              two workgroups per CU (used when 256-row blocks leave CUs idle).
+ *   VALU:      fp32 or bf16, D in {16, 32, 64, 128}; one lane per query,
+ *              fp32 vector arithmetic (the fp32 path, and small head dims). */
 typedef enum fa_variant {
   FA_VARIANT_AUTO = 0,
-  FA_VARIANT_MFMA_Q64 = 1,
-  FA_VARIANT_MFMA_Q32 = 2,
+  FA_VARIANT_MFMA_B256 = 1,
+  FA_VARIANT_MFMA_B128 = 2,
   FA_VARIANT_VALU = 3
 } fa_variant;
 
@@ -77,7 +79,8 @@ typedef enum fa_variant {
  *   causal    nonzero: key j visible to row i iff j <= i (the diagonal included)
  *   scale     multiplies q.k; used as given (callers normally pass 1/sqrt(D))
  *   dtype     FA_DTYPE_BF16 or FA_DTYPE_FP32; softmax state and accumulation
- *             are fp32 either way, and bf16 probabilities feed the P.V product
+ *             are fp32 either way; on the matrix-core variants the
+ *             probabilities are rounded to bf16 before the P.V product
  *   stream    hipStream_t or NULL
  *
  * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED (also when

@@ -77,9 +77,9 @@ def test_unsupported_dtype_and_variant():
     assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, 7) == fa.FA_ERR_UNSUPPORTED
     # the matrix-core variants are bf16-only and D in {64, 128}
     assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_FP32,
-                         variant=fa.FA_VARIANT_MFMA_Q64) == fa.FA_ERR_UNSUPPORTED
+                         variant=fa.FA_VARIANT_MFMA_B256) == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 32, True, 0.1, fa.FA_DTYPE_BF16,
-                         variant=fa.FA_VARIANT_MFMA_Q32) == fa.FA_ERR_UNSUPPORTED
+                         variant=fa.FA_VARIANT_MFMA_B128) == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16, variant=42) == fa.FA_ERR_UNSUPPORTED
 
 
@@ -90,8 +90,8 @@ def test_size_limits_rejected():
 
 def test_variant_selection():
     bf16, f32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP32
-    assert fa.select_variant(8, 32, 8192, 128, bf16) == fa.FA_VARIANT_MFMA_Q64
-    assert fa.select_variant(1, 32, 1024, 128, bf16) == fa.FA_VARIANT_MFMA_Q32
+    assert fa.select_variant(8, 32, 8192, 128, bf16) == fa.FA_VARIANT_MFMA_B256
+    assert fa.select_variant(1, 32, 1024, 128, bf16) == fa.FA_VARIANT_MFMA_B128
     assert fa.select_variant(1, 1, 64, 16, f32) == fa.FA_VARIANT_VALU
     assert fa.select_variant(1, 1, 64, 16, bf16) == fa.FA_VARIANT_VALU
     assert fa.select_variant(1, 1, 64, 128, f32) == fa.FA_VARIANT_VALU
@@ -103,7 +103,7 @@ def test_variant_selection():
 @pytest.mark.parametrize("causal", [True, False])
 def test_scheduler_tile_counts(S, causal):
     """The library's per-head tile count equals the causal block rule's closed form."""
-    for variant, bq, bk in ((fa.FA_VARIANT_MFMA_Q64, 256, 64), (fa.FA_VARIANT_MFMA_Q32, 128, 64),
+    for variant, bq, bk in ((fa.FA_VARIANT_MFMA_B256, 256, 64), (fa.FA_VARIANT_MFMA_B128, 128, 64),
                             (fa.FA_VARIANT_VALU, 64, 32)):
         assert fa.tiles_per_head(S, causal, variant) == causal_kv_tiles(S, bq, bk, causal)
     assert fa.tiles_per_head(S, causal, 0) == 0

@@ -60,7 +60,7 @@ def test_page_worked_example_fp32():
 
 # ---------------------------------------------------------------- full checks at oracle-sized shapes
 
-@pytest.mark.parametrize("variant", ["auto", "mfma_q64", "mfma_q32", "valu"])
+@pytest.mark.parametrize("variant", ["auto", "mfma_b256", "mfma_b128", "valu"])
 @pytest.mark.parametrize("causal", [True, False])
 def test_b1_h32_s1024_d128(variant, causal):
     case(f"bf16 1x32x1024x128 causal={causal} variant={variant}, full oracle")
@@ -72,7 +72,7 @@ def test_b1_h32_s1024_d128(variant, causal):
 
 
 @pytest.mark.parametrize("S", [1, 2, 31, 63, 64, 65, 127, 129, 255, 257, 333, 1000])
-@pytest.mark.parametrize("variant", ["mfma_q64", "mfma_q32", "valu"])
+@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128", "valu"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_ragged_lengths_bf16(S, variant, D):
     case(f"bf16 2x3x{S}x{D} causal variant={variant}")
@@ -107,7 +107,7 @@ def test_bf16_small_head_dims(D):
 
 # ---------------------------------------------------------------- scale and score-range edge cases
 
-@pytest.mark.parametrize("variant", ["mfma_q64", "mfma_q32", "valu"])
+@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128", "valu"])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0])
 def test_scale_values(variant, scale):
     case(f"bf16 1x2x300x128 scale={scale} variant={variant}")
@@ -118,7 +118,7 @@ def test_scale_values(variant, scale):
                  f"scale {scale} {variant}")
 
 
-@pytest.mark.parametrize("variant", ["mfma_q64", "mfma_q32"])
+@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128"])
 def test_wide_score_range(variant):
     """Q, K ~ uniform(-4, 4): score std ~5, so the running max jumps and alpha rescales often."""
     case(f"bf16 1x4x1000x128 Q,K uniform(-4,4) variant={variant}")
@@ -137,7 +137,7 @@ def test_increasing_scores_force_rescale():
     k = (torch.arange(S, device="cuda", dtype=torch.float32) / S * 3.0)[None, None, :, None].expand(1, 1, S, D)
     _, _, v = device_inputs(1, 1, S, D, seed=5)
     q, k = q.to(torch.bfloat16).contiguous(), k.to(torch.bfloat16).contiguous()
-    for variant in ("mfma_q64", "mfma_q32", "valu"):
+    for variant in ("mfma_b256", "mfma_b128", "valu"):
         o, lse = run_fwd(q, k, v, causal=True, variant=variant)
         ref_o, ref_l = oracle_on(q, k, v, True, scale_of(D))
         assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, torch.bfloat16,
@@ -216,10 +216,10 @@ def test_deterministic_and_stream_independent():
 
 def test_variants_agree():
     """Two tilings (256- and 128-query blocks) give the same result within rounding."""
-    case("bf16 2x4x777x128 mfma_q64 vs mfma_q32")
+    case("bf16 2x4x777x128 mfma_b256 vs mfma_b128")
     q, k, v = device_inputs(2, 4, 777, 128, seed=3)
-    oa, la = run_fwd(q, k, v, variant="mfma_q64")
-    ob, lb = run_fwd(q, k, v, variant="mfma_q32")
+    oa, la = run_fwd(q, k, v, variant="mfma_b256")
+    ob, lb = run_fwd(q, k, v, variant="mfma_b128")
     assert (oa.float() - ob.float()).abs().max().item() <= 1e-2
     assert (la - lb).abs().max().item() <= 1e-5
 

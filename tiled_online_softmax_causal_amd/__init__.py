@@ -18,8 +18,8 @@ LIBRARY_PATH = os.path.join(_PKG, "libfa_mi355x.so")
 
 FA_DTYPE_FP32, FA_DTYPE_BF16 = 0, 1
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-FA_VARIANT_AUTO, FA_VARIANT_MFMA_Q64, FA_VARIANT_MFMA_Q32, FA_VARIANT_VALU = 0, 1, 2, 3
-VARIANTS = {"auto": 0, "mfma_q64": 1, "mfma_q32": 2, "valu": 3}
+FA_VARIANT_AUTO, FA_VARIANT_MFMA_B256, FA_VARIANT_MFMA_B128, FA_VARIANT_VALU = 0, 1, 2, 3
+VARIANTS = {"auto": 0, "mfma_b256": 1, "mfma_b128": 2, "valu": 3}
 
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_fwd_select_variant", "fa_fwd_tiles_per_head",
@@ -80,8 +80,10 @@ def tiles_per_head(S: int, causal: bool, variant: int) -> int:
 def kernel_name(variant: int, D: int, causal: bool) -> str:
     """Name prefix of the kernel a variant launches (as profilers print it)."""
     c = "true" if causal else "false"
-    if variant in (FA_VARIANT_MFMA_Q64, FA_VARIANT_MFMA_Q32):
-        return f"fa::attn_fwd_mfma_bf16<{D}, {2 if variant == FA_VARIANT_MFMA_Q64 else 1}, {c}>"
+    if variant == FA_VARIANT_MFMA_B256:
+        return f"fa::pp::attn_fwd_pingpong<{D}, {c}>"
+    if variant == FA_VARIANT_MFMA_B128:
+        return f"fa::attn_fwd_mfma_bf16<{D}, 1, {c}>"
     if variant == FA_VARIANT_VALU:
         return "fa::attn_fwd_valu<"
     raise ValueError(f"unknown variant {variant}")

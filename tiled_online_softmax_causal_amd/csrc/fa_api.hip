@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "fa_fwd_pingpong.h"
 #include "fa_mfma_bf16.h"
 #include "fa_valu.h"
 
@@ -22,12 +23,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int64_t mfma_block_q(int variant) { return variant == FA_VARIANT_MFMA_Q64 ? 4 * 64 : 4 * 32; }
+int64_t mfma_block_q(int variant) { return variant == FA_VARIANT_MFMA_B256 ? fa::pp::kBQ : 4 * 32; }
 
 bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
   switch (variant) {
-    case FA_VARIANT_MFMA_Q64:
-    case FA_VARIANT_MFMA_Q32:
+    case FA_VARIANT_MFMA_B256:
+    case FA_VARIANT_MFMA_B128:
       return dtype == FA_DTYPE_BF16 && (D == 64 || D == 128);
     case FA_VARIANT_VALU:
       return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP32) && (D == 16 || D == 32 || D == 64 || D == 128);
@@ -36,13 +37,13 @@ bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
   }
 }
 
-// Shape-only choice: bf16 with D 64/128 runs on the matrix cores, 64 queries per
-// wave unless that leaves fewer than two workgroups per CU, where the 32-query
+// Shape-only choice: bf16 with D 64/128 runs on the matrix cores, in 256-row
+// workgroups (one per CU) unless that leaves CUs idle, where the 128-row
 // variant doubles the grid.
 int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
   if (dtype == FA_DTYPE_BF16 && (D == 64 || D == 128)) {
-    const int64_t wgs = B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_Q64));
-    return wgs >= 2 * 256 ? FA_VARIANT_MFMA_Q64 : FA_VARIANT_MFMA_Q32;
+    const int64_t wgs = B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256));
+    return wgs >= 256 ? FA_VARIANT_MFMA_B256 : FA_VARIANT_MFMA_B128;
   }
   if (variant_covers(FA_VARIANT_VALU, D, dtype)) return FA_VARIANT_VALU;
   return -1;
@@ -67,6 +68,27 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* o, flo
   else
     hipLaunchKernelGGL((fa::attn_fwd_mfma_bf16<D, NSUB, false>), dim3((unsigned)grid), dim3(fa::kThreads), 0,
                        stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)BH, c, negate_q, xcd_group);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                           int64_t S, int causal, float scale, hipStream_t stream) {
+  const int64_t n_qb = ceil_div(S, fa::pp::kBQ);
+  const int64_t grid = BH * n_qb;
+  const int xcd_group = (BH % kNumXcd) == 0;
+  const float c = std::fabs(scale) * kLog2e;
+  const int negate_q = scale < 0.f;
+  const auto* Q = static_cast<const uint16_t*>(q);
+  const auto* K = static_cast<const uint16_t*>(k);
+  const auto* V = static_cast<const uint16_t*>(v);
+  auto* O = static_cast<uint16_t*>(o);
+  if (causal)
+    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, true>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
+                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, c, negate_q, xcd_group);
+  else
+    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, false>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
+                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, c, negate_q, xcd_group);
   return hipGetLastError();
 }
 
@@ -111,7 +133,7 @@ int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype d
 
 int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant) {
   int64_t bq, bk;
-  if (variant == FA_VARIANT_MFMA_Q64 || variant == FA_VARIANT_MFMA_Q32) {
+  if (variant == FA_VARIANT_MFMA_B256 || variant == FA_VARIANT_MFMA_B128) {
     bq = mfma_block_q(variant);
     bk = fa::kBK;
   } else if (variant == FA_VARIANT_VALU) {
@@ -152,9 +174,9 @@ fa_status fa_fwd_variant(const void* q, const void* k, const void* v, void* o, f
   if (variant == FA_VARIANT_VALU) {
     err = dtype == FA_DTYPE_FP32 ? launch_valu_d<float>(q, k, v, o, lse, BH, S, D, causal, scale, st)
                                  : launch_valu_d<uint16_t>(q, k, v, o, lse, BH, S, D, causal, scale, st);
-  } else if (variant == FA_VARIANT_MFMA_Q64) {
-    err = D == 128 ? launch_mfma<128, 2>(q, k, v, o, lse, BH, S, causal, scale, st)
-                   : launch_mfma<64, 2>(q, k, v, o, lse, BH, S, causal, scale, st);
+  } else if (variant == FA_VARIANT_MFMA_B256) {
+    err = D == 128 ? launch_pingpong<128>(q, k, v, o, lse, BH, S, causal, scale, st)
+                   : launch_pingpong<64>(q, k, v, o, lse, BH, S, causal, scale, st);
   } else {
     err = D == 128 ? launch_mfma<128, 1>(q, k, v, o, lse, BH, S, causal, scale, st)
                    : launch_mfma<64, 1>(q, k, v, o, lse, BH, S, causal, scale, st);
