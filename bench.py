@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma_b256", "mfma_b128", "valu"])
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run --steps plain device copies of MIB MiB (the "
+                         "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -132,9 +135,20 @@ def main():
     from tiled_online_softmax_causal_amd.costmodel import algorithmic_bytes, attention_flops
     from workloads import uniform_qkv_device
 
-    B, H, S, D, causal, cpu_heads = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return
+
+    B, H, S, D, causal, cpu_heads = WORKLOADS[args.workload]
     log(f"[bench] {fa.version()} on {torch.cuda.get_device_name(dev)}; workload {args.workload}")
     q, k, v = uniform_qkv_device(B, H, S, D, seed=args.seed, dtype=torch.bfloat16, device=dev)
     o = torch.empty_like(q)

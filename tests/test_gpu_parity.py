@@ -144,6 +144,40 @@ def test_increasing_scores_force_rescale():
                      f"growing {variant}")
 
 
+@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128", "valu"])
+def test_scores_outgrow_fp32_range(variant):
+    """Scores that rise by ~1.85 (base 2) per key: within one 64-key tile they grow
+    by ~118, so exponentiating against the previous tile's maximum would overflow
+    fp32.  Kernels that keep a stale maximum must detect that and rescale."""
+    case(f"bf16 1x2x700x128 scale=1 growing scores, variant={variant}")
+    S, D = 700, 128
+    q = torch.full((1, 2, S, D), 0.5, device="cuda")
+    k = (torch.arange(S, device="cuda", dtype=torch.float32) * 0.02)[None, None, :, None].expand(1, 2, S, D)
+    _, _, v = device_inputs(1, 2, S, D, seed=6)
+    q, k = q.to(torch.bfloat16).contiguous(), k.to(torch.bfloat16).contiguous()
+    o, lse = run_fwd(q, k, v, causal=True, scale=1.0, variant=variant)
+    ref_o, ref_l = oracle_on(q, k, v, True, 1.0)
+    assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, torch.bfloat16,
+                 f"outgrow {variant}")
+
+
+@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128"])
+def test_scores_outgrow_fp32_range_masked(variant):
+    """As above but decreasing keys: the largest scores sit in the first tile and
+    the causal mask hides the end of each diagonal tile, so rows whose visible
+    keys are all far below the running maximum must still come out right."""
+    case(f"bf16 1x1x333x128 scale=1 shrinking scores, variant={variant}")
+    S, D = 333, 128
+    q = torch.full((1, 1, S, D), 0.5, device="cuda")
+    k = ((S - torch.arange(S, device="cuda", dtype=torch.float32)) * 0.02)[None, None, :, None].expand(1, 1, S, D)
+    _, _, v = device_inputs(1, 1, S, D, seed=8)
+    q, k = q.to(torch.bfloat16).contiguous(), k.to(torch.bfloat16).contiguous()
+    o, lse = run_fwd(q, k, v, causal=True, scale=1.0, variant=variant)
+    ref_o, ref_l = oracle_on(q, k, v, True, 1.0)
+    assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, torch.bfloat16,
+                 f"shrink {variant}")
+
+
 # ---------------------------------------------------------------- the benchmark's workloads, sampled
 
 def _sampled_check(B, H, S, D, causal, bh_idx, n_rows, variant="auto"):

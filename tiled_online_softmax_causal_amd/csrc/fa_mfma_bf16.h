@@ -26,10 +26,10 @@
 //    per CU) would otherwise cap the matrix cores near their peak / 1.
 //  * K and V tiles are staged HBM -> registers -> LDS, double buffered, one
 //    barrier per tile.  LDS rows are XOR-swizzled in 16-byte chunks,
-//    chunk' = chunk ^ f(row) with f(row) = 2*(row%4) + (row/4)%2, so the 8
-//    lanes of a 128-bit K read (8 consecutive rows) and the 16 lanes of a
-//    64-bit transposed V read (4 consecutive rows x 32 bytes) hit distinct
-//    banks.
+//    chunk' = chunk ^ f(row) with f(row) = 4*(row%4) + (row/4)%4, so the 16
+//    lanes of a 128-bit K read (16 consecutive rows) and the 32 lanes of a
+//    64-bit transposed V read (4 rows x 64 bytes) hit distinct banks of a
+//    64-bank LDS.
 //  * The softmax runs in the base-2 domain: c = scale * log2(e) is folded into
 //    one FMA per score, exp is v_exp_f32, and the log-sum-exp is converted back
 //    to natural log at the end.  A negative scale is handled by negating Q at
@@ -71,12 +71,16 @@ struct TileGeo {
   static_assert(kBK * kChunks % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
-__device__ __forceinline__ int lds_swizzle(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// XOR key of a row's 16-byte chunks, masked to the row's chunk count.
+template <int D>
+__device__ __forceinline__ int lds_swizzle(int row) {
+  return (((row & 3) << 2) | ((row >> 2) & 3)) & (TileGeo<D>::kChunks - 1);
+}
 
 // Byte offset of logical 16-byte chunk `chunk` of row `row` in a swizzled tile.
 template <int D>
 __device__ __forceinline__ int lds_chunk_offset(int row, int chunk) {
-  return row * TileGeo<D>::kRowBytes + ((chunk ^ lds_swizzle(row)) << 4);
+  return row * TileGeo<D>::kRowBytes + ((chunk ^ lds_swizzle<D>(row)) << 4);
 }
 
 __device__ __forceinline__ float wave_max_halves(float x) {
@@ -126,7 +130,7 @@ struct TileStager {
       const int cidx = i * kThreads + tid;
       const int row = cidx / TileGeo<D>::kChunks;
       const int pch = cidx % TileGeo<D>::kChunks;
-      const int lch = pch ^ lds_swizzle(row);
+      const int lch = pch ^ lds_swizzle<D>(row);
       const int grow = min(kv0 + row, S - 1);
       const size_t off = (size_t)grow * D + lch * 8;
       kr[i] = *reinterpret_cast<const u32x4_t*>(Kh + off);

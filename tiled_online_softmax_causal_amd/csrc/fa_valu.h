@@ -7,8 +7,8 @@
 // (every lane of the wave reads the same K/V row, an LDS broadcast), the
 // causal rule ending the walk at the block's last row, a per-row running
 // maximum / sum / accumulator, and a row with no visible key in a tile left
-// untouched.  Scores, softmax and accumulation are fp32; exp is taken in
-// base 2 with scale * log2(e) folded into the score.
+// untouched.  Scores, softmax and accumulation are fp32; each q.k is summed in
+// four partial sums and then scaled once by scale * log2(e) (exp in base 2).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kValuBQ) void attn_fwd_valu(const T* __restrict__ Q
     const T* src = Q + head_off + (size_t)min(qi, S - 1) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) {
-      qr[c] = to_f32<T>(src[c]) * c_log2;  // scores come out in the base-2 domain
+      qr[c] = to_f32<T>(src[c]);
       acc[c] = 0.f;
     }
   }
@@ -75,9 +75,12 @@ __global__ __launch_bounds__(kValuBQ) void attn_fwd_valu(const T* __restrict__ Q
     float tmax = -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < kValuBK; ++j) {
-      float x = 0.f;
+      // q.k in four interleaved partial sums (shorter rounding chains), then
+      // one multiply by scale*log2(e) into the base-2 domain
+      float x4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < D; ++c) x = __builtin_fmaf(qr[c], ks[j][c], x);
+      for (int c = 0; c < D; ++c) x4[c & 3] = __builtin_fmaf(qr[c], ks[j][c], x4[c & 3]);
+      const float x = ((x4[0] + x4[1]) + (x4[2] + x4[3])) * c_log2;
       const int kj = kv0 + j;
       const bool visible = kj < S && (!CAUSAL || kj <= qi);
       s[j] = visible ? x : -__builtin_inff();
