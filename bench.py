@@ -75,6 +75,49 @@ def measured_traffic(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
+def _counter_mean(csv_path: str, counter: str, kernel_substr: str) -> float:
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for a kernel matching {kernel_substr!r} in {csv_path}")
+    return sum(vals) / len(vals)
+
+
+def record_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
+                   copy_write_csv: str, copy_mib: int):
+    """Turn four rocprofv3 --pmc counter_collection.csv files into HBM bytes per launch.
+
+    FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same
+    counter reports for a plain device copy of copy_mib MiB (read and written once).
+    The result is stored with a hash of the kernel sources, so it is reported only
+    while the kernel is unchanged.
+    """
+    fetch_kib = _counter_mean(fetch_csv, "FETCH_SIZE", "attn_fwd")
+    write_kib = _counter_mean(write_csv, "WRITE_SIZE", "attn_fwd")
+    copy_fetch_kib = _counter_mean(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    copy_write_kib = _counter_mean(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    true_kib = copy_mib * 1024.0
+    f_fetch, f_write = true_kib / copy_fetch_kib, true_kib / copy_write_kib
+    hbm = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("source_sha256") != kernel_source_hash():
+        rec = {"source_sha256": kernel_source_hash(), "workloads": {}}
+    rec["workloads"][workload] = {
+        "hbm_bytes_per_launch": round(hbm),
+        "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
+        "copy_calibration": {"mib": copy_mib, "fetch_kib": copy_fetch_kib, "write_kib": copy_write_kib,
+                             "fetch_factor": f_fetch, "write_factor": f_write},
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec["workloads"][workload]))
+
+
 def cpu_baseline(q, k, v, o, lse, n_heads: int, causal: bool, scale: float):
     """Time the fp64 oracle on n_heads whole heads (every row); check the GPU on them."""
     import numpy as np
@@ -122,7 +165,14 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run --steps plain device copies of MIB MiB (the "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="store HBM bytes per launch for --workload from rocprofv3 --pmc counter CSVs "
+                         "(attention run and --copy-calibration run), then exit")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size used for --copy-calibration")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic, args.copy_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the forward pass shards over (batch, head) with no communication; run one process per GPU)",
