@@ -1,0 +1,66 @@
+"""Guard for the inline-assembly global->LDS copies of the ping-pong kernel.
+
+The copies set M0 (the LDS destination) right before each
+global_load_lds_dwordx4 from inline assembly.  That is only sound while no
+compiler-generated instruction in the kernel uses M0.  This test compiles the
+library to gfx950 assembly (no GPU needed) and checks, in every kernel that
+issues such copies, that each write of M0 is immediately followed by the copy
+and that no other instruction that reads M0 implicitly appears.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from tiled_online_softmax_causal_amd import build as fa_build
+
+# instructions that read M0 implicitly on gfx9 (besides the LDS copies themselves)
+M0_READERS = re.compile(r"\b(s_sendmsg|s_movrel|v_movrel|ds_gws|v_interp|s_set_gpr_idx|ds_.*_addtid|"
+                        r"buffer_load_\w+\s.*\blds\b|global_load_lds_(?!dwordx4))")
+
+
+@pytest.fixture(scope="module")
+def device_asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "fa.s"
+    cmd = [fa_build.hipcc(), "--offload-arch=gfx950", "--cuda-device-only", "-S", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans",
+           "-I", os.path.join(fa_build.ROOT, "include"), "-I", fa_build.CSRC,
+           os.path.join(fa_build.CSRC, "fa_api.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return out.read_text()
+
+
+def _kernels(asm: str):
+    """(name, instruction lines) for every kernel body in the assembly."""
+    out, name, body = [], None, []
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            name, body = m.group(1), []
+            continue
+        if name is None:
+            continue
+        text = line.split(";")[0].strip()
+        if text and not text.startswith("."):
+            body.append(text)
+        if text.startswith("s_endpgm"):
+            out.append((name, body))
+            name = None
+    return out
+
+
+def test_m0_is_only_the_lds_copy_destination(device_asm):
+    kernels = _kernels(device_asm)
+    copying = [(n, b) for n, b in kernels if any(i.startswith("global_load_lds_dwordx4") for i in b)]
+    assert copying, "no kernel issues global->LDS copies"
+    assert any("attn_fwd_pingpong" in n for n, _ in copying)
+    for name, body in copying:
+        for k, ins in enumerate(body):
+            assert not M0_READERS.search(ins), f"{name}: unexpected M0 reader: {ins}"
+            if re.search(r"\bm0\b", ins):
+                assert re.match(r"s_mov_b32 m0, s\d+$", ins), f"{name}: M0 written by: {ins}"
+                assert body[k + 1].startswith("global_load_lds_dwordx4"), f"{name}: M0 write not followed by a copy"
+            if ins.startswith("global_load_lds_dwordx4"):
+                assert re.match(r"s_mov_b32 m0, s\d+$", body[k - 1]), f"{name}: copy without its M0 write"

@@ -22,13 +22,12 @@
 // each phase.
 //
 // Data movement.  Group 0 carries the K tiles (64 keys) and group 1 the V
-// tiles: K_{t+1} is loaded HBM -> registers during group 0's matrix phase 2t,
-// V_t during group 1's softmax phase 2t, and both are written to LDS at the end
-// of phase 2t+1 into the half of a double buffer whose previous tile was last
-// read in phase 2t-1.  Each wave's loads are spread through its phase's work.
-// LDS rows are padded (K by 16 bytes, V by 64 bytes) so the 128-bit K reads
-// and the 64-bit transposed V reads are free of bank conflicts on the 64-bank
-// LDS, and every read address is one per-lane base plus immediate offsets.
+// tiles, copied HBM -> LDS directly (global_load_lds, no register staging)
+// into 3-slot rings: K_{t+2} is started at the end of group 0's matrix phase 2t
+// and V_{t+1} at the end of group 1's matrix phase 2t+1, three to four phases
+// before their first reader, while the MFMAs issued before them drain.  LDS
+// rows are XOR-swizzled in 16-byte chunks so the 128-bit K reads and the
+// 64-bit transposed V reads are free of bank conflicts on the 64-bank LDS.
 //
 // Register layout (v_mfma_f32_32x32x16_bf16).  Scores are formed transposed,
 // S^T = K . Q^T, so each lane owns ONE query (column lane%32) and half of the
@@ -77,27 +76,41 @@ constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBQ = kQW * kWaves;       // query rows per workgroup
 constexpr int kBK = 64;                 // keys per tile
 constexpr int kAhead = 8;               // MFMAs between an operand's LDS read and its use
+constexpr int kStages = 3;              // depth of the K and V rings in LDS
 constexpr float kOverflowSum = 0x1p64f; // a tile sum above this forces a rescale
 constexpr float kLn2 = 0.693147180559945309f;
 
-// LDS tiles are row-major with padded rows.  K rows carry 16 pad bytes: the 16
-// rows of one 16-lane group of a 128-bit K read then start on 16 different
-// 4-bank groups.  V rows carry 64 pad bytes: the 4 rows x 64 bytes of one
-// 32-lane transposed V read then cover all 64 banks once.
+// LDS tiles are row-major, D*2 bytes per row, with the 16-byte chunks of each
+// row XOR-swizzled by swz(row) (masked to the row's chunk count).  For d = 128
+// the 16 rows of one 16-lane group of a 128-bit K read get 16 different keys,
+// and the 4 rows x 4 chunks of one 32-lane transposed V read land in 16
+// different chunk columns, so neither read has bank conflicts on the 64-bank
+// LDS.  Rows stay contiguous, as the direct global->LDS loads need.
 template <int D>
 struct Geo {
   static_assert(D == 64 || D == 128, "matrix-core path covers D = 64 and 128");
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = kRowBytes / 16;               // 16-byte chunks per row
-  static constexpr int kKStride = kRowBytes + 16;               // LDS bytes per K row
-  static constexpr int kVStride = kRowBytes + 64;               // LDS bytes per V row
-  static constexpr int kKTileBytes = kBK * kKStride;
-  static constexpr int kVTileBytes = kBK * kVStride;
-  static constexpr int kLdsBytes = 2 * (kKTileBytes + kVTileBytes);  // K[2], V[2]
+  static constexpr int kTileBytes = kBK * kRowBytes;            // one K or V tile
+  static constexpr int kLdsBytes = 2 * kStages * kTileBytes;    // K ring, V ring
   static constexpr int kLoads = kBK * kChunks / kGroupThreads;   // 16-byte loads per thread per tile
   static constexpr int kRowsPerLoad = kGroupThreads / kChunks;   // tile rows covered by one load step
   static_assert(kBK * kChunks % kGroupThreads == 0, "a tile must split evenly over a 4-wave group");
 };
+
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return (((row & 3) << 2) | ((row >> 2) & 3)) & (Geo<D>::kChunks - 1);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; a counter left at its maximum is not waited for).
+template <int N>
+constexpr int waitcnt_vm() {  // at most N vector-memory loads outstanding
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);  // all LDS operations complete
 
 __device__ __forceinline__ float max_halves(float x) {
   // lanes l and l^32 hold the two key halves of the same query
@@ -110,13 +123,12 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Workgroup barrier that orders LDS only: outstanding global prefetches stay in
-// flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+// Workgroup barrier that is also a compiler barrier for memory operations but
+// waits for nothing by itself: the global->LDS copies in flight stay in flight
+// across it.  Whatever must have landed before it is waited for explicitly by
+// the caller (s_waitcnt), and every LDS read a wave issues is consumed, hence
+// complete, within the phase that issues it.
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Workgroup id -> (bh, query block).  Heaviest query blocks first (under the
 // causal rule block qb visits qb+1 key ranges).  When the head count is a
@@ -136,18 +148,16 @@ __device__ __forceinline__ void schedule_block(int wg, int n_qb, int xcd_group, 
 
 // Issue order of a matrix phase: MFMA items 0..NPV-1 are the P.V products (two
 // LDS reads each), items NPV.. the score products (one LDS read each).  The
-// reads of item i + kAhead are issued right after MFMA i, and one tile load is
-// issued every FSTEP MFMAs while NLOAD remain.
+// reads of item i + kAhead are issued right after MFMA i.
 template <int NPV, int N>
 constexpr int reads_of(int i) {
   return i < NPV ? 2 : (i < N ? 1 : 0);
 }
-template <int NPV, int N, int FSTEP, int NLOAD, int I>
+template <int NPV, int N, int I>
 __device__ __forceinline__ void schedule_item() {
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA I
   if constexpr (reads_of<NPV, N>(I + kAhead) > 0)
     __builtin_amdgcn_sched_group_barrier(0x100, reads_of<NPV, N>(I + kAhead), 0);
-  if constexpr (NLOAD > 0 && I % FSTEP == 0 && I / FSTEP < NLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
 }
 template <int NPV, int N>
 constexpr int first_reads() {
@@ -155,10 +165,10 @@ constexpr int first_reads() {
   for (int i = 0; i < kAhead; ++i) r += reads_of<NPV, N>(i);
   return r;
 }
-template <int NPV, int N, int FSTEP, int NLOAD, int... I>
+template <int NPV, int N, int... I>
 __device__ __forceinline__ void schedule_matrix_phase(std::integer_sequence<int, I...>) {
   __builtin_amdgcn_sched_group_barrier(0x100, first_reads<NPV, N>(), 0);
-  (schedule_item<NPV, N, FSTEP, NLOAD, I>(), ...);
+  (schedule_item<NPV, N, I>(), ...);
 }
 
 template <int D, bool CAUSAL>
@@ -168,7 +178,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     int xcd_group) {
   using G = Geo<D>;
   using T_ = std::true_type;
-  using F_ = std::false_type;
   constexpr int DS = D / 16;  // k-steps of the score MFMA
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int NL = G::kLoads;
@@ -217,89 +226,110 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   // tiles this wave takes part in (its rows see keys below min(S, q0w + 32))
   const int n_w = q0w >= S ? 0 : (CAUSAL ? min(n_tiles, (min(q0w + kQW, S) - 1) / kBK + 1) : n_tiles);
 
-  // ---- staging: HBM -> registers -> LDS.  Thread gtid of the carrying group
-  // owns 16-byte chunks gtid, gtid + 256, ... (row-major) of its tensor's tile.
-  // Rows past the end of the sequence re-read row S-1 (their scores are masked).
+  // ---- staging: HBM -> LDS directly (global_load_lds, 16 bytes per lane).
+  // Thread gtid of the carrying group fills 16-byte slots gtid, gtid + 256, ...
+  // (row-major) of its tensor's tile; the source is the logical chunk that the
+  // swizzle puts in that slot.  Rows past the end of the sequence re-read row
+  // S-1 (their scores are masked).  Tile t lives in ring slot t % kStages.
   const int gtid = tid & (kGroupThreads - 1);
-  const int g_row = gtid / G::kChunks, g_chunk = gtid % G::kChunks;
-  const uint16_t* const src_g = (grp == 0 ? K : V) + head_off + g_chunk * 8;
-  const int stride_g = grp == 0 ? G::kKStride : G::kVStride;
-  u32x4_t stg[NL];
-  auto fetch_one = [&](int i, int t) {
-    const int grow = min(t * kBK + g_row + i * G::kRowsPerLoad, S - 1);
-    stg[i] = *reinterpret_cast<const u32x4_t*>(src_g + grow * D);
-  };
-  auto deposit = [&](char* buf) {
-    char* dst = buf + g_row * stride_g + g_chunk * 16;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) *reinterpret_cast<u32x4_t*>(dst + i * G::kRowsPerLoad * stride_g) = stg[i];
-  };
+  const int gwave = wave & 3;
+  const int g_row = gtid / G::kChunks;
+  const int g_lch = (gtid % G::kChunks) ^ swz<D>(g_row);  // same for every load step
+  const uint16_t* const src_g = (grp == 0 ? K : V) + head_off;
   char* const kbuf0 = lds;
-  char* const vbuf0 = lds + 2 * G::kKTileBytes;
-  // per-lane read bases: K row col (+32 per key block), 16 bytes per half;
-  // V rows 4*half + u/4 (+16 per k-step), columns 16*(quad%2) + 4*(u%4)
-  const int k_lane = col * G::kKStride + half * 16;
-  const int v_lane = (4 * half + (u >> 2)) * G::kVStride + (16 * (quad & 1) + 4 * (u & 3)) * 2;
+  char* const vbuf0 = lds + kStages * G::kTileBytes;
+  char* const ring_g = grp == 0 ? kbuf0 : vbuf0;
+  auto stage_of = [](int t) { return (t + kStages) % kStages; };
+  // Start the copy of tile t_src into the ring slot of tile t_dst (all load
+  // steps).  The copy is issued from inline assembly so that the compiler does
+  // not track it: it would otherwise drain every copy in flight before each
+  // transposed LDS read it cannot prove disjoint.  The ordering it would have
+  // enforced is kept explicitly instead (s_waitcnt vmcnt before the barrier
+  // that publishes a slot, slots refilled only after their last reader).  M0
+  // carries the LDS destination and is set right before each copy; nothing
+  // else in this kernel uses M0 (a CPU test checks the generated code).
+  auto fetch_tile = [&](int t_src, int t_dst) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int grow = min(t_src * kBK + g_row + i * G::kRowsPerLoad, S - 1);
+      const uint16_t* src = src_g + grow * D + g_lch * 8;
+      const unsigned dst = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(
+          ring_g + stage_of(t_dst) * G::kTileBytes + (i * kGroupThreads + gwave * 64) * 16);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see the comment above
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(src) : "m0");
+#pragma clang diagnostic pop
+    }
+  };
+  // per-lane read offsets within a tile.  K: row 32*kb + col, logical chunk
+  // 2*ds + half.  V (transposed read): rows 16*ks + 4*half + u/4 (+8 for the
+  // upper k-slots), logical chunk 4*db + 2*(quad%2) + (u%4)/2, byte 8*(u%2).
+  int k_off[DS], v_off_lo[DB], v_off_hi[DB];
+  {
+    const int sk = swz<D>(col);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) k_off[ds] = col * G::kRowBytes + (((2 * ds + half) ^ sk) << 4);
+    const int vr = 4 * half + (u >> 2);
+    const int s_lo = swz<D>(vr), s_hi = swz<D>(vr + 8);
+    const int c_l = 2 * (quad & 1) + ((u & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      v_off_lo[db] = vr * G::kRowBytes + (((4 * db + c_l) ^ s_lo) << 4) + 8 * (u & 1);
+      v_off_hi[db] = (vr + 8) * G::kRowBytes + (((4 * db + c_l) ^ s_hi) << 4) + 8 * (u & 1);
+    }
+  }
 
   // ---- matrix phase t: O^T += V_{t-1}^T P_{t-1}^T (4 accumulators, k-step
   // outer), then S_t^T = K_t Q^T (2 accumulators, alternating).
-  auto matrix_body = [&](auto pv_c, auto sc_c, auto load_c, int t, int t_load) {
-    constexpr bool PV = decltype(pv_c)::value, SC = decltype(sc_c)::value, LOAD = decltype(load_c)::value;
+  auto matrix_body = [&](auto pv_c, auto sc_c, int t) {
+    constexpr bool PV = decltype(pv_c)::value, SC = decltype(sc_c)::value;
     constexpr int NPV = PV ? DB * 4 : 0, NSC = SC ? DS * 2 : 0, N = NPV + NSC;
-    constexpr int FSTEP = N / NL > 0 ? N / NL : 1;
-    const char* Vl = vbuf0 + ((t - 1) & 1) * G::kVTileBytes + v_lane;
-    const char* Kl = kbuf0 + (t & 1) * G::kKTileBytes + k_lane;
+    const char* Vl = vbuf0 + stage_of(t - 1) * G::kTileBytes;
+    const char* Kl = kbuf0 + stage_of(t) * G::kTileBytes;
     // the matrix-core wave issues first; the softmax wave on the same SIMD
     // fills the issue slots the MFMAs leave free
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < (N > 0 ? N : NL); ++i) {
-      if (LOAD && i % FSTEP == 0 && i / FSTEP < NL) fetch_one(i / FSTEP, t_load);
+    for (int i = 0; i < N; ++i) {
       if (i < NPV) {
         const int ks = i / DB, db = i % DB;
-        const char* vp = Vl + 16 * ks * G::kVStride + 64 * db;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vp);
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 8 * G::kVStride));
+        const char* vp = Vl + 16 * ks * G::kRowBytes;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + v_off_lo[db]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + v_off_hi[db]));
         const bf16x8_t av = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
                                                     __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], oacc[db], 0, 0, 0);
       } else if (i < N) {
         const int j = i - NPV, ds = j / 2, kb = j % 2;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kKStride + 32 * ds);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
       }
     }
-    if constexpr (N > 0)
-      schedule_matrix_phase<NPV, N, FSTEP, LOAD ? NL : 0>(std::make_integer_sequence<int, N>{});
+    if constexpr (N > 0) schedule_matrix_phase<NPV, N>(std::make_integer_sequence<int, N>{});
     __builtin_amdgcn_s_setprio(0);
   };
-  // Group 0 passes load = true: it carries K_{t+1} during matrix phase t.  Every
-  // wave runs the same full body in every matrix phase, which keeps the loop's
-  // register allocation simple.  Where a product is not needed its result is
-  // harmless: at t = 0 the probabilities are zero and the V buffer half read
-  // was zero-filled, and once a wave is past its last tile (t > n_w) its
+  // Every wave runs the same full body in every matrix phase, which keeps the
+  // loop's register allocation simple.  Where a product is not needed its
+  // result is harmless: at t = 0 the probabilities are zero and the V ring slot
+  // read was zero-filled, and once a wave is past its last tile (t > n_w) its
   // skipped softmax phases zero the probabilities, so the P.V product adds
-  // exactly 0; scores for t >= n_w are computed but never used.
-  auto matrix_phase = [&](int t, auto load_c) {
-    const int t_load = min(t + 1, n_tiles - 1);  // the last phase re-reads a tile it does not deposit
-    matrix_body(T_{}, T_{}, load_c, t, t_load);
+  // exactly 0; scores for t >= n_w are computed but never used.  After its
+  // MFMAs are issued the wave starts its group's next tile copy: K_{t+2}
+  // (group 0) or V_{t+1} (group 1).  Past the last tile the copy re-reads the
+  // last tile into a slot nobody reads, which keeps the wait counts uniform.
+  auto matrix_phase = [&](int t) {
+    matrix_body(T_{}, T_{}, t);
+    const int t_dst = grp == 0 ? t + 2 : t + 1;
+    fetch_tile(min(t_dst, n_tiles - 1), t_dst);
   };
 
-  // ---- softmax phase t: S_t -> bf16 P_t, running max / sum.  Group 1 passes
-  // load = true: it carries V_{t+1} during softmax phase t.
-  auto softmax_phase = [&](int t, auto load_c) {
-    constexpr bool LOAD = decltype(load_c)::value;
-    const int t_load = min(t + 1, n_tiles - 1);
+  // ---- softmax phase t: S_t -> bf16 P_t, running max / sum
+  auto softmax_phase = [&](int t) {
     if (t < 0 || t >= n_w) {
-      if (LOAD) {
-#pragma unroll
-        for (int i = 0; i < NL; ++i) fetch_one(i, t_load);
-      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) pb[ks] = (bf16x8_t){};
       return;
     }
-    if (LOAD) fetch_one(0, t_load);
     const int kv0 = t * kBK;
     const int qi = q0w + col;
     float c_t = c_log2;
@@ -316,7 +346,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           sacc[kb][r] = hidden ? -__builtin_inff() : sacc[kb][r] * c_log2;
         }
     }
-    if (LOAD && NL > 1) fetch_one(1, t_load);
     // exponentiate against the running (possibly stale) maximum; all but the
     // first tile try that directly and fall back to the exact update only when
     // a probability could approach fp32 overflow
@@ -360,45 +389,50 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       m_run = m_new;
       exponentiate();
     }
-    if (LOAD) {
-#pragma unroll
-      for (int i = 2; i < NL; ++i) fetch_one(i, t_load);
-    }
     l_run += rs;
   };
 
-  // ---- prologue: K_0 into LDS (group 0 carries K); zero the V buffer half that
-  // the first matrix phase reads with zero probabilities
+  // ---- prologue: group 0 starts K_0 and K_1, group 1 starts V_0 and zero-fills
+  // the V ring slot that the first matrix phase reads with zero probabilities
   if (grp == 0) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) fetch_one(i, 0);
-    deposit(kbuf0);
+    fetch_tile(0, 0);
+    fetch_tile(min(1, n_tiles - 1), 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
   } else {
-    char* v1 = vbuf0 + G::kVTileBytes;
-    for (int off = gtid * 16; off < G::kVTileBytes; off += kGroupThreads * 16)
-      *reinterpret_cast<u32x4_t*>(v1 + off) = (u32x4_t){0u, 0u, 0u, 0u};
+    fetch_tile(0, 0);
+    char* v_prev = vbuf0 + stage_of(-1) * G::kTileBytes;
+    for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
+      *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the zeros are in LDS
   }
-  lds_barrier();
+  phase_barrier();
 
   // ---- 2 * (n_tiles + 1) phases, one barrier each.  The two groups run the
   // same phases with their roles swapped; each has its own straight loop.
+  // Group 0 starts K_{t+2} at the end of phase 2t, group 1 starts V_{t+1} at
+  // the end of phase 2t+1.  Before the barrier that closes phase 2t+1 each
+  // group waits until only its latest copy is in flight, so K_{t+1} and V_t
+  // have landed before their first readers (phases 2t+2 and 2t+2).  A ring slot
+  // is refilled only after the phase that last reads its previous tile.
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
-      matrix_phase(t, T_{});  // phase 2t; loads K_{t+1}
-      lds_barrier();
-      softmax_phase(t, F_{});  // phase 2t + 1
-      if (t + 1 < n_tiles) deposit(kbuf0 + ((t + 1) & 1) * G::kKTileBytes);
-      lds_barrier();
+      matrix_phase(t);  // phase 2t; starts K_{t+2}
+      phase_barrier();
+      softmax_phase(t);  // phase 2t + 1
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
+      phase_barrier();
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
-      softmax_phase(t - 1, T_{});  // phase 2t; loads V_t
-      lds_barrier();
-      matrix_phase(t, F_{});  // phase 2t + 1
-      if (t < n_tiles) deposit(vbuf0 + (t & 1) * G::kVTileBytes);
-      lds_barrier();
+      softmax_phase(t - 1);  // phase 2t
+      phase_barrier();
+      matrix_phase(t);  // phase 2t + 1; starts V_{t+1}
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
+      phase_barrier();
     }
   }
+  // no global->LDS copy may still be writing when the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), lse = ln2 * (m + log2 l)
   const int qi = q0w + col;
