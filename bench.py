@@ -159,7 +159,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_b256", "mfma_b128", "valu"])
+    from tiled_online_softmax_causal_amd import VARIANTS
+    ap.add_argument("--variant", default="auto", choices=list(VARIANTS))
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

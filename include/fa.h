@@ -60,12 +60,15 @@ typedef enum fa_status {
  *   MFMA_B128: bf16, D in {64, 128}; 128-row query blocks, 4 waves of 32 rows,
  *              two workgroups per CU (used when 256-row blocks leave CUs idle).
  *   VALU:      fp32 or bf16, D in {16, 32, 64, 128}; one lane per query,
- *              fp32 vector arithmetic (the fp32 path, and small head dims). */
+ *              fp32 vector arithmetic (the fp32 path, and small head dims).
+ *   MFMA_B256_K128: as MFMA_B256 with 128-key tiles (64-key tiles otherwise):
+ *              twice the work per phase, half the barriers, 2-slot rings. */
 typedef enum fa_variant {
   FA_VARIANT_AUTO = 0,
   FA_VARIANT_MFMA_B256 = 1,
   FA_VARIANT_MFMA_B128 = 2,
-  FA_VARIANT_VALU = 3
+  FA_VARIANT_VALU = 3,
+  FA_VARIANT_MFMA_B256_K128 = 4
 } fa_variant;
 
 /*

@@ -28,6 +28,10 @@ from workloads import page_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
 
+# the matrix-core kernels: 256-query ping-pong with 64- and 128-key tiles, and
+# the 128-query four-wave kernel
+MFMA = ["mfma_b256", "mfma_b256_k128", "mfma_b128"]
+
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -60,7 +64,7 @@ def test_page_worked_example_fp32():
 
 # ---------------------------------------------------------------- full checks at oracle-sized shapes
 
-@pytest.mark.parametrize("variant", ["auto", "mfma_b256", "mfma_b128", "valu"])
+@pytest.mark.parametrize("variant", ["auto", *MFMA, "valu"])
 @pytest.mark.parametrize("causal", [True, False])
 def test_b1_h32_s1024_d128(variant, causal):
     case(f"bf16 1x32x1024x128 causal={causal} variant={variant}, full oracle")
@@ -72,7 +76,7 @@ def test_b1_h32_s1024_d128(variant, causal):
 
 
 @pytest.mark.parametrize("S", [1, 2, 31, 63, 64, 65, 127, 129, 255, 257, 333, 1000])
-@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128", "valu"])
+@pytest.mark.parametrize("variant", [*MFMA, "valu"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_ragged_lengths_bf16(S, variant, D):
     case(f"bf16 2x3x{S}x{D} causal variant={variant}")
@@ -107,7 +111,7 @@ def test_bf16_small_head_dims(D):
 
 # ---------------------------------------------------------------- scale and score-range edge cases
 
-@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128", "valu"])
+@pytest.mark.parametrize("variant", [*MFMA, "valu"])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0])
 def test_scale_values(variant, scale):
     case(f"bf16 1x2x300x128 scale={scale} variant={variant}")
@@ -118,7 +122,7 @@ def test_scale_values(variant, scale):
                  f"scale {scale} {variant}")
 
 
-@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128"])
+@pytest.mark.parametrize("variant", MFMA)
 def test_wide_score_range(variant):
     """Q, K ~ uniform(-4, 4): score std ~5, so the running max jumps and alpha rescales often."""
     case(f"bf16 1x4x1000x128 Q,K uniform(-4,4) variant={variant}")
@@ -137,14 +141,14 @@ def test_increasing_scores_force_rescale():
     k = (torch.arange(S, device="cuda", dtype=torch.float32) / S * 3.0)[None, None, :, None].expand(1, 1, S, D)
     _, _, v = device_inputs(1, 1, S, D, seed=5)
     q, k = q.to(torch.bfloat16).contiguous(), k.to(torch.bfloat16).contiguous()
-    for variant in ("mfma_b256", "mfma_b128", "valu"):
+    for variant in (*MFMA, "valu"):
         o, lse = run_fwd(q, k, v, causal=True, variant=variant)
         ref_o, ref_l = oracle_on(q, k, v, True, scale_of(D))
         assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, torch.bfloat16,
                      f"growing {variant}")
 
 
-@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128", "valu"])
+@pytest.mark.parametrize("variant", [*MFMA, "valu"])
 def test_scores_outgrow_fp32_range(variant):
     """Scores that rise by ~1.85 (base 2) per key: within one 64-key tile they grow
     by ~118, so exponentiating against the previous tile's maximum would overflow
@@ -161,7 +165,7 @@ def test_scores_outgrow_fp32_range(variant):
                  f"outgrow {variant}")
 
 
-@pytest.mark.parametrize("variant", ["mfma_b256", "mfma_b128"])
+@pytest.mark.parametrize("variant", MFMA)
 def test_scores_outgrow_fp32_range_masked(variant):
     """As above but decreasing keys: the largest scores sit in the first tile and
     the causal mask hides the end of each diagonal tile, so rows whose visible
@@ -199,10 +203,11 @@ def test_b1_h32_s4096_sampled(causal):
     _sampled_check(1, 32, 4096, 128, causal, list(range(32)), 48)
 
 
-def test_b8_h32_s8192_sampled():
-    case("bf16 8x32x8192x128 causal (benchmark launch), 4 heads x 256 rows")
+@pytest.mark.parametrize("variant", ["auto", "mfma_b256", "mfma_b256_k128"])
+def test_b8_h32_s8192_sampled(variant):
+    case(f"bf16 8x32x8192x128 causal (benchmark launch) variant={variant}, 4 heads x 256 rows")
     bh = [0 * 32 + 0, 3 * 32 + 17, 5 * 32 + 4, 7 * 32 + 31]
-    _sampled_check(8, 32, 8192, 128, True, bh, 256)
+    _sampled_check(8, 32, 8192, 128, True, bh, 256, variant=variant)
     torch.cuda.empty_cache()
 
 
@@ -248,12 +253,13 @@ def test_deterministic_and_stream_independent():
     assert torch.equal(o0, o2) and torch.equal(l0, l2)
 
 
-def test_variants_agree():
-    """Two tilings (256- and 128-query blocks) give the same result within rounding."""
-    case("bf16 2x4x777x128 mfma_b256 vs mfma_b128")
+@pytest.mark.parametrize("other", ["mfma_b128", "mfma_b256_k128"])
+def test_variants_agree(other):
+    """Different tilings and schedules give the same result within rounding."""
+    case(f"bf16 2x4x777x128 mfma_b256 vs {other}")
     q, k, v = device_inputs(2, 4, 777, 128, seed=3)
     oa, la = run_fwd(q, k, v, variant="mfma_b256")
-    ob, lb = run_fwd(q, k, v, variant="mfma_b128")
+    ob, lb = run_fwd(q, k, v, variant=other)
     assert (oa.float() - ob.float()).abs().max().item() <= 1e-2
     assert (la - lb).abs().max().item() <= 1e-5
 

@@ -13,8 +13,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa_mi355x.so")
 SOURCES = [os.path.join(CSRC, "fa_api.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("fa_mfma_bf16.h", "fa_valu.h")] + [
-    os.path.join(ROOT, "include", "fa.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

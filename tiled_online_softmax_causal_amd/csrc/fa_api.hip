@@ -23,12 +23,17 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int64_t mfma_block_q(int variant) { return variant == FA_VARIANT_MFMA_B256 ? fa::pp::kBQ : 4 * 32; }
+int64_t mfma_block_q(int variant) {
+  return variant == FA_VARIANT_MFMA_B256 || variant == FA_VARIANT_MFMA_B256_K128 ? fa::pp::kBQ : 4 * 32;
+}
+
+int64_t mfma_block_k(int variant) { return variant == FA_VARIANT_MFMA_B256_K128 ? 128 : fa::kBK; }
 
 bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
   switch (variant) {
     case FA_VARIANT_MFMA_B256:
     case FA_VARIANT_MFMA_B128:
+    case FA_VARIANT_MFMA_B256_K128:
       return dtype == FA_DTYPE_BF16 && (D == 64 || D == 128);
     case FA_VARIANT_VALU:
       return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP32) && (D == 16 || D == 32 || D == 64 || D == 128);
@@ -38,12 +43,12 @@ bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
 }
 
 // Shape-only choice: bf16 with D 64/128 runs on the matrix cores, in 256-row
-// workgroups (one per CU) unless that leaves CUs idle, where the 128-row
-// variant doubles the grid.
+// workgroups (one per CU) with 128-key tiles unless that leaves CUs idle,
+// where the 128-row variant doubles the grid.
 int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
   if (dtype == FA_DTYPE_BF16 && (D == 64 || D == 128)) {
-    const int64_t wgs = B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256));
-    return wgs >= 256 ? FA_VARIANT_MFMA_B256 : FA_VARIANT_MFMA_B128;
+    const int64_t wgs = B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128));
+    return wgs >= 256 ? FA_VARIANT_MFMA_B256_K128 : FA_VARIANT_MFMA_B128;
   }
   if (variant_covers(FA_VARIANT_VALU, D, dtype)) return FA_VARIANT_VALU;
   return -1;
@@ -71,7 +76,7 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* o, flo
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int BK>
 hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
                            int64_t S, int causal, float scale, hipStream_t stream) {
   const int64_t n_qb = ceil_div(S, fa::pp::kBQ);
@@ -84,10 +89,10 @@ hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o,
   const auto* V = static_cast<const uint16_t*>(v);
   auto* O = static_cast<uint16_t*>(o);
   if (causal)
-    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, true>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
+    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
                        stream, Q, K, V, O, lse, (int)S, (int)n_qb, c, negate_q, xcd_group);
   else
-    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, false>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
+    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
                        stream, Q, K, V, O, lse, (int)S, (int)n_qb, c, negate_q, xcd_group);
   return hipGetLastError();
 }
@@ -133,9 +138,10 @@ int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype d
 
 int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant) {
   int64_t bq, bk;
-  if (variant == FA_VARIANT_MFMA_B256 || variant == FA_VARIANT_MFMA_B128) {
+  if (variant == FA_VARIANT_MFMA_B256 || variant == FA_VARIANT_MFMA_B128 ||
+      variant == FA_VARIANT_MFMA_B256_K128) {
     bq = mfma_block_q(variant);
-    bk = fa::kBK;
+    bk = mfma_block_k(variant);
   } else if (variant == FA_VARIANT_VALU) {
     bq = fa::kValuBQ;
     bk = fa::kValuBK;
@@ -174,9 +180,12 @@ fa_status fa_fwd_variant(const void* q, const void* k, const void* v, void* o, f
   if (variant == FA_VARIANT_VALU) {
     err = dtype == FA_DTYPE_FP32 ? launch_valu_d<float>(q, k, v, o, lse, BH, S, D, causal, scale, st)
                                  : launch_valu_d<uint16_t>(q, k, v, o, lse, BH, S, D, causal, scale, st);
+  } else if (variant == FA_VARIANT_MFMA_B256_K128) {
+    err = D == 128 ? launch_pingpong<128, 128>(q, k, v, o, lse, BH, S, causal, scale, st)
+                   : launch_pingpong<64, 128>(q, k, v, o, lse, BH, S, causal, scale, st);
   } else if (variant == FA_VARIANT_MFMA_B256) {
-    err = D == 128 ? launch_pingpong<128>(q, k, v, o, lse, BH, S, causal, scale, st)
-                   : launch_pingpong<64>(q, k, v, o, lse, BH, S, causal, scale, st);
+    err = D == 128 ? launch_pingpong<128, 64>(q, k, v, o, lse, BH, S, causal, scale, st)
+                   : launch_pingpong<64, 64>(q, k, v, o, lse, BH, S, causal, scale, st);
   } else {
     err = D == 128 ? launch_mfma<128, 1>(q, k, v, o, lse, BH, S, causal, scale, st)
                    : launch_mfma<64, 1>(q, k, v, o, lse, BH, S, causal, scale, st);

@@ -1,0 +1,91 @@
+// Device helpers shared by the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+namespace common {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr float kLn2 = 0.693147180559945309f;
+
+// lanes l and l^32 hold the two key halves of the same query
+__device__ __forceinline__ float max_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Workgroup barrier that is also a compiler barrier for memory operations but
+// waits for nothing by itself: global->LDS copies in flight stay in flight
+// across it.  Whatever must have landed before it is waited for explicitly by
+// the caller (s_waitcnt), and every LDS read a wave issues is consumed, hence
+// complete, before the barrier that follows it.
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; a counter left at its maximum is not waited for).
+template <int N>
+constexpr int waitcnt_vm() {  // at most N vector-memory loads outstanding
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);  // all LDS operations complete
+
+// XOR key of a row's 16-byte chunks for rows of `chunks` chunks (a power of
+// two).  With 16 chunks per row (d = 128) the 16 rows of one 16-lane group of
+// a 128-bit K read get 16 different keys, and the 4 rows x 4 chunks of one
+// 32-lane transposed V read land in 16 different chunk columns, so neither
+// read has bank conflicts on the 64-bank LDS.
+template <int CHUNKS>
+__device__ __forceinline__ int swz(int row) {
+  return (((row & 3) << 2) | ((row >> 2) & 3)) & (CHUNKS - 1);
+}
+
+// Workgroup id -> (bh, query block).  Heaviest query blocks first (under the
+// causal rule block qb visits qb+1 key ranges).  When the head count is a
+// multiple of 8, every query block of a head is placed on one XCD (workgroups
+// are dispatched round-robin over the 8 XCDs), so the head's K/V stream is
+// shared in that XCD's L2 by the blocks running there at the same time.
+__device__ __forceinline__ void schedule_block(int wg, int n_qb, int xcd_group, int& bh, int& qb) {
+  if (xcd_group) {
+    const int xcd = wg & 7, idx = wg >> 3;
+    bh = (idx / n_qb) * 8 + xcd;
+    qb = n_qb - 1 - idx % n_qb;
+  } else {
+    bh = wg / n_qb;
+    qb = n_qb - 1 - wg % n_qb;
+  }
+}
+
+// Start one 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane
+// l's 16 bytes land at lds_dst + 16*l (lds_dst is wave-uniform).  Issued from
+// inline assembly so that the compiler does not track it: it would otherwise
+// drain every copy in flight before each transposed LDS read it cannot prove
+// disjoint.  Callers keep the ordering explicitly (s_waitcnt vmcnt before the
+// barrier that publishes a slot; slots refilled only after their last reader).
+// M0 carries the LDS destination and is set right before the copy; nothing
+// else in these kernels uses M0 (a CPU test checks the generated code).
+__device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_dst) {
+  const unsigned dst = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds_dst;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see the comment above
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(src) : "m0");
+#pragma clang diagnostic pop
+}
+
+}  // namespace common
+}  // namespace fa

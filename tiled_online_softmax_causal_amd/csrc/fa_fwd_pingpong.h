@@ -15,19 +15,22 @@
 //     phase 2t+1   group 0: softmax phase t     group 1: matrix phase t
 //
 // where the matrix phase t issues O^T += V_{t-1}^T P_{t-1}^T and then
-// S_t^T = K_t Q^T on the matrix cores (32 MFMAs for d = 128) and the softmax
-// phase t turns S_t into bf16 probabilities on the vector ALUs.  Every SIMD
-// thus holds one wave feeding its matrix core and one wave doing the
+// S_t^T = K_t Q^T on the matrix cores (32 MFMAs per 64 keys for d = 128) and
+// the softmax phase t turns S_t into bf16 probabilities on the vector ALUs.
+// Every SIMD thus holds one wave feeding its matrix core and one wave doing the
 // exponentials, the two kinds of work overlap, and one workgroup barrier closes
-// each phase.
+// each phase.  A key tile is BK = 64 or 128 keys; the longer tile halves the
+// barriers and per-phase bookkeeping per unit of work.
 //
-// Data movement.  Group 0 carries the K tiles (64 keys) and group 1 the V
-// tiles, copied HBM -> LDS directly (global_load_lds, no register staging)
-// into 3-slot rings: K_{t+2} is started at the end of group 0's matrix phase 2t
-// and V_{t+1} at the end of group 1's matrix phase 2t+1, three to four phases
-// before their first reader, while the MFMAs issued before them drain.  LDS
-// rows are XOR-swizzled in 16-byte chunks so the 128-bit K reads and the
-// 64-bit transposed V reads are free of bank conflicts on the 64-bank LDS.
+// Data movement.  Group 0 carries the K tiles and group 1 the V tiles, copied
+// HBM -> LDS directly (global_load_lds, no register staging) into rings of
+// kStages slots.  With BK = 64 (3 slots) K_{t+2} is started at the end of
+// group 0's matrix phase 2t and V_{t+1} at the end of group 1's matrix phase
+// 2t+1, three to four phases before their first reader.  With BK = 128 (2
+// slots, 128 KB of LDS for d = 128) K_{t+1} and V_t are started when phase 2t
+// begins, two phases before their first reader.  LDS rows are XOR-swizzled in
+// 16-byte chunks so the 128-bit K reads and the 64-bit transposed V reads are
+// free of bank conflicts on the 64-bank LDS.
 //
 // Register layout (v_mfma_f32_32x32x16_bf16).  Scores are formed transposed,
 // S^T = K . Q^T, so each lane owns ONE query (column lane%32) and half of the
@@ -35,8 +38,9 @@
 // and row sum are lane-local plus one v_permlane32_swap.  The fp32 scores,
 // exponentiated and packed to bf16, are already the B operand of
 // O^T = V^T . P^T; V^T comes from LDS through ds_read_b64_tr_b16 in the
-// matching key order.  The MFMA operands read from LDS run four MFMAs ahead of
-// their use (a pinned issue order), so LDS latency hides behind the matrix core.
+// matching key order.  The MFMA operands read from LDS run eight MFMAs ahead
+// of their use (a pinned issue order), so LDS latency hides behind the matrix
+// core.
 //
 // Softmax.  Base 2: c = scale*log2(e) is folded into one FMA per score and exp
 // is v_exp_f32.  The maximum only guards exp2 against overflow, so it is
@@ -56,29 +60,20 @@
 #include <type_traits>
 #include <utility>
 
+#include "fa_common.h"
+
 namespace fa {
 namespace pp {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+using namespace fa::common;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupThreads = kThreads / 2;
 constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBQ = kQW * kWaves;       // query rows per workgroup
-constexpr int kBK = 64;                 // keys per tile
 constexpr int kAhead = 8;               // MFMAs between an operand's LDS read and its use
-constexpr int kStages = 3;              // depth of the K and V rings in LDS
 constexpr float kOverflowSum = 0x1p64f; // a tile sum above this forces a rescale
-constexpr float kLn2 = 0.693147180559945309f;
 
 // LDS tiles are row-major, D*2 bytes per row, with the 16-byte chunks of each
 // row XOR-swizzled by swz(row) (masked to the row's chunk count).  For d = 128
@@ -86,65 +81,20 @@ constexpr float kLn2 = 0.693147180559945309f;
 // and the 4 rows x 4 chunks of one 32-lane transposed V read land in 16
 // different chunk columns, so neither read has bank conflicts on the 64-bank
 // LDS.  Rows stay contiguous, as the direct global->LDS loads need.
-template <int D>
+template <int D, int BK>
 struct Geo {
   static_assert(D == 64 || D == 128, "matrix-core path covers D = 64 and 128");
+  static_assert(BK == 64 || BK == 128, "key tiles of 64 or 128 keys");
+  static constexpr int kStages = BK == 64 ? 3 : 2;               // depth of the K and V rings
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = kRowBytes / 16;               // 16-byte chunks per row
-  static constexpr int kTileBytes = kBK * kRowBytes;            // one K or V tile
+  static constexpr int kTileBytes = BK * kRowBytes;             // one K or V tile
   static constexpr int kLdsBytes = 2 * kStages * kTileBytes;    // K ring, V ring
-  static constexpr int kLoads = kBK * kChunks / kGroupThreads;   // 16-byte loads per thread per tile
+  static constexpr int kLoads = BK * kChunks / kGroupThreads;    // 16-byte loads per thread per tile
   static constexpr int kRowsPerLoad = kGroupThreads / kChunks;   // tile rows covered by one load step
-  static_assert(kBK * kChunks % kGroupThreads == 0, "a tile must split evenly over a 4-wave group");
+  static_assert(BK * kChunks % kGroupThreads == 0, "a tile must split evenly over a 4-wave group");
+  static_assert(kLdsBytes <= 160 * 1024, "rings must fit the 160 KB LDS");
 };
-
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  return (((row & 3) << 2) | ((row >> 2) & 3)) & (Geo<D>::kChunks - 1);
-}
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
-// 6:4, lgkmcnt in 11:8; a counter left at its maximum is not waited for).
-template <int N>
-constexpr int waitcnt_vm() {  // at most N vector-memory loads outstanding
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);  // all LDS operations complete
-
-__device__ __forceinline__ float max_halves(float x) {
-  // lanes l and l^32 hold the two key halves of the same query
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-
-__device__ __forceinline__ float sum_halves(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-// Workgroup barrier that is also a compiler barrier for memory operations but
-// waits for nothing by itself: the global->LDS copies in flight stay in flight
-// across it.  Whatever must have landed before it is waited for explicitly by
-// the caller (s_waitcnt), and every LDS read a wave issues is consumed, hence
-// complete, within the phase that issues it.
-__device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Workgroup id -> (bh, query block).  Heaviest query blocks first (under the
-// causal rule block qb visits qb+1 key ranges).  When the head count is a
-// multiple of 8, every query block of a head is placed on one XCD (workgroups
-// are dispatched round-robin over the 8 XCDs), so the head's K/V stream is
-// shared in that XCD's L2 by the blocks running there at the same time.
-__device__ __forceinline__ void schedule_block(int wg, int n_qb, int xcd_group, int& bh, int& qb) {
-  if (xcd_group) {
-    const int xcd = wg & 7, idx = wg >> 3;
-    bh = (idx / n_qb) * 8 + xcd;
-    qb = n_qb - 1 - idx % n_qb;
-  } else {
-    bh = wg / n_qb;
-    qb = n_qb - 1 - wg % n_qb;
-  }
-}
 
 // Issue order of a matrix phase: MFMA items 0..NPV-1 are the P.V products (two
 // LDS reads each), items NPV.. the score products (one LDS read each).  The
@@ -171,16 +121,19 @@ __device__ __forceinline__ void schedule_matrix_phase(std::integer_sequence<int,
   (schedule_item<NPV, N, I>(), ...);
 }
 
-template <int D, bool CAUSAL>
+template <int D, int BK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int S, int n_qb, float c_log2, int negate_q,
     int xcd_group) {
-  using G = Geo<D>;
+  using G = Geo<D, BK>;
   using T_ = std::true_type;
-  constexpr int DS = D / 16;  // k-steps of the score MFMA
-  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int DS = D / 16;   // k-steps of the score MFMA
+  constexpr int DB = D / 32;   // 32-row blocks of O^T
+  constexpr int KB = BK / 32;  // 32-key blocks of S^T
+  constexpr int KS = BK / 16;  // k-steps of the P.V MFMA
   constexpr int NL = G::kLoads;
+  constexpr int kStages = G::kStages;
 
   __shared__ __attribute__((aligned(16))) char lds[G::kLdsBytes];
 
@@ -215,16 +168,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   f32x16_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
-  f32x16_t sacc[2];
-  bf16x8_t pb[4];
+  f32x16_t sacc[KB];
+  bf16x8_t pb[KS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) pb[ks] = (bf16x8_t){};
+  for (int ks = 0; ks < KS; ++ks) pb[ks] = (bf16x8_t){};
   float m_run = -__builtin_inff(), l_run = 0.f;
 
   const int kv_end = CAUSAL ? min(S, q0 + kBQ) : S;
-  const int n_tiles = (kv_end + kBK - 1) / kBK;
+  const int n_tiles = (kv_end + BK - 1) / BK;
   // tiles this wave takes part in (its rows see keys below min(S, q0w + 32))
-  const int n_w = q0w >= S ? 0 : (CAUSAL ? min(n_tiles, (min(q0w + kQW, S) - 1) / kBK + 1) : n_tiles);
+  const int n_w = q0w >= S ? 0 : (CAUSAL ? min(n_tiles, (min(q0w + kQW, S) - 1) / BK + 1) : n_tiles);
 
   // ---- staging: HBM -> LDS directly (global_load_lds, 16 bytes per lane).
   // Thread gtid of the carrying group fills 16-byte slots gtid, gtid + 256, ...
@@ -234,31 +187,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   const int gtid = tid & (kGroupThreads - 1);
   const int gwave = wave & 3;
   const int g_row = gtid / G::kChunks;
-  const int g_lch = (gtid % G::kChunks) ^ swz<D>(g_row);  // same for every load step
+  const int g_lch = (gtid % G::kChunks) ^ swz<G::kChunks>(g_row);  // same for every load step
   const uint16_t* const src_g = (grp == 0 ? K : V) + head_off;
   char* const kbuf0 = lds;
   char* const vbuf0 = lds + kStages * G::kTileBytes;
   char* const ring_g = grp == 0 ? kbuf0 : vbuf0;
   auto stage_of = [](int t) { return (t + kStages) % kStages; };
-  // Start the copy of tile t_src into the ring slot of tile t_dst (all load
-  // steps).  The copy is issued from inline assembly so that the compiler does
-  // not track it: it would otherwise drain every copy in flight before each
-  // transposed LDS read it cannot prove disjoint.  The ordering it would have
-  // enforced is kept explicitly instead (s_waitcnt vmcnt before the barrier
-  // that publishes a slot, slots refilled only after their last reader).  M0
-  // carries the LDS destination and is set right before each copy; nothing
-  // else in this kernel uses M0 (a CPU test checks the generated code).
+  // Start the copy of tile t_src into the ring slot of tile t_dst (all load steps).
   auto fetch_tile = [&](int t_src, int t_dst) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int grow = min(t_src * kBK + g_row + i * G::kRowsPerLoad, S - 1);
-      const uint16_t* src = src_g + grow * D + g_lch * 8;
-      const unsigned dst = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(
-          ring_g + stage_of(t_dst) * G::kTileBytes + (i * kGroupThreads + gwave * 64) * 16);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see the comment above
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(src) : "m0");
-#pragma clang diagnostic pop
+      const int grow = min(t_src * BK + g_row + i * G::kRowsPerLoad, S - 1);
+      copy16_to_lds(src_g + grow * D + g_lch * 8,
+                    ring_g + stage_of(t_dst) * G::kTileBytes + (i * kGroupThreads + gwave * 64) * 16);
     }
   };
   // per-lane read offsets within a tile.  K: row 32*kb + col, logical chunk
@@ -266,11 +207,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   // upper k-slots), logical chunk 4*db + 2*(quad%2) + (u%4)/2, byte 8*(u%2).
   int k_off[DS], v_off_lo[DB], v_off_hi[DB];
   {
-    const int sk = swz<D>(col);
+    const int sk = swz<G::kChunks>(col);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) k_off[ds] = col * G::kRowBytes + (((2 * ds + half) ^ sk) << 4);
     const int vr = 4 * half + (u >> 2);
-    const int s_lo = swz<D>(vr), s_hi = swz<D>(vr + 8);
+    const int s_lo = swz<G::kChunks>(vr), s_hi = swz<G::kChunks>(vr + 8);
     const int c_l = 2 * (quad & 1) + ((u & 3) >> 1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -279,11 +220,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     }
   }
 
-  // ---- matrix phase t: O^T += V_{t-1}^T P_{t-1}^T (4 accumulators, k-step
-  // outer), then S_t^T = K_t Q^T (2 accumulators, alternating).
+  // ---- matrix phase t: O^T += V_{t-1}^T P_{t-1}^T (DB accumulators, k-step
+  // outer), then S_t^T = K_t Q^T (KB accumulators, alternating).
   auto matrix_body = [&](auto pv_c, auto sc_c, int t) {
     constexpr bool PV = decltype(pv_c)::value, SC = decltype(sc_c)::value;
-    constexpr int NPV = PV ? DB * 4 : 0, NSC = SC ? DS * 2 : 0, N = NPV + NSC;
+    constexpr int NPV = PV ? DB * KS : 0, NSC = SC ? DS * KB : 0, N = NPV + NSC;
     const char* Vl = vbuf0 + stage_of(t - 1) * G::kTileBytes;
     const char* Kl = kbuf0 + stage_of(t) * G::kTileBytes;
     // the matrix-core wave issues first; the softmax wave on the same SIMD
@@ -300,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
                                                     __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], oacc[db], 0, 0, 0);
       } else if (i < N) {
-        const int j = i - NPV, ds = j / 2, kb = j % 2;
+        const int j = i - NPV, ds = j / KB, kb = j % KB;
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
       }
@@ -313,32 +254,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   // result is harmless: at t = 0 the probabilities are zero and the V ring slot
   // read was zero-filled, and once a wave is past its last tile (t > n_w) its
   // skipped softmax phases zero the probabilities, so the P.V product adds
-  // exactly 0; scores for t >= n_w are computed but never used.  After its
-  // MFMAs are issued the wave starts its group's next tile copy: K_{t+2}
-  // (group 0) or V_{t+1} (group 1).  Past the last tile the copy re-reads the
-  // last tile into a slot nobody reads, which keeps the wait counts uniform.
+  // exactly 0; scores for t >= n_w are computed but never used.  With three
+  // ring slots, after its MFMAs are issued the wave starts its group's next
+  // tile copy: K_{t+2} (group 0) or V_{t+1} (group 1).  Past the last tile the
+  // copy re-reads the last tile into a slot nobody reads, which keeps the wait
+  // counts uniform.
   auto matrix_phase = [&](int t) {
     matrix_body(T_{}, T_{}, t);
-    const int t_dst = grp == 0 ? t + 2 : t + 1;
-    fetch_tile(min(t_dst, n_tiles - 1), t_dst);
+    if constexpr (kStages == 3) {
+      const int t_dst = grp == 0 ? t + 2 : t + 1;
+      fetch_tile(min(t_dst, n_tiles - 1), t_dst);
+    }
   };
 
   // ---- softmax phase t: S_t -> bf16 P_t, running max / sum
   auto softmax_phase = [&](int t) {
     if (t < 0 || t >= n_w) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) pb[ks] = (bf16x8_t){};
+      for (int ks = 0; ks < KS; ++ks) pb[ks] = (bf16x8_t){};
       return;
     }
-    const int kv0 = t * kBK;
+    const int kv0 = t * BK;
     const int qi = q0w + col;
     float c_t = c_log2;
     // Tiles that straddle the diagonal or run past S move to the base-2 domain
     // here, so a hidden score is a plain -inf even when the scale is 0.
-    if ((CAUSAL && kv0 + kBK - 1 > q0w) || kv0 + kBK > S) {
+    if ((CAUSAL && kv0 + BK - 1 > q0w) || kv0 + BK > S) {
       c_t = 1.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kj = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -354,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
       rs = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         const int kb = ks >> 1, r0 = 8 * (ks & 1);
         bf16x8_t p8;
 #pragma unroll
@@ -378,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     if (exact) {
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
       const float m_new = fmaxf(m_run, max_halves(mx) * c_t);
@@ -392,14 +336,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     l_run += rs;
   };
 
-  // ---- prologue: group 0 starts K_0 and K_1, group 1 starts V_0 and zero-fills
-  // the V ring slot that the first matrix phase reads with zero probabilities
+  // ---- prologue: group 0 starts K_0 (and, with three slots, K_1); group 1
+  // zero-fills the V ring slot that the first matrix phase reads with zero
+  // probabilities (and, with three slots, starts V_0)
   if (grp == 0) {
     fetch_tile(0, 0);
-    fetch_tile(min(1, n_tiles - 1), 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
+    if constexpr (kStages == 3) {
+      fetch_tile(min(1, n_tiles - 1), 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+    }
   } else {
-    fetch_tile(0, 0);
+    if constexpr (kStages == 3) fetch_tile(0, 0);
     char* v_prev = vbuf0 + stage_of(-1) * G::kTileBytes;
     for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
       *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
@@ -409,25 +358,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
 
   // ---- 2 * (n_tiles + 1) phases, one barrier each.  The two groups run the
   // same phases with their roles swapped; each has its own straight loop.
-  // Group 0 starts K_{t+2} at the end of phase 2t, group 1 starts V_{t+1} at
-  // the end of phase 2t+1.  Before the barrier that closes phase 2t+1 each
-  // group waits until only its latest copy is in flight, so K_{t+1} and V_t
-  // have landed before their first readers (phases 2t+2 and 2t+2).  A ring slot
-  // is refilled only after the phase that last reads its previous tile.
+  // Three slots: group 0 starts K_{t+2} at the end of phase 2t, group 1
+  // starts V_{t+1} at the end of phase 2t+1, and before the barrier that
+  // closes phase 2t+1 each group waits until only its latest copy is in
+  // flight.  Two slots: K_{t+1} (group 0) and V_t (group 1) start when phase
+  // 2t begins, into the slots last read in phase 2t-1, and have landed at the
+  // barrier that closes phase 2t+1.  Either way K_{t+1} and V_t are in LDS
+  // before their first reader, phase 2t+2, and a ring slot is refilled only
+  // after the phase that last reads its previous tile.  (Past the last tile a
+  // K copy re-reads the last tile into a slot that holds only junk scores.)
+  constexpr int kInFlight = kStages == 3 ? NL : 0;
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
-      matrix_phase(t);  // phase 2t; starts K_{t+2}
+      if constexpr (kStages == 2)
+        if (t < n_tiles) fetch_tile(min(t + 1, n_tiles - 1), t + 1);
+      matrix_phase(t);  // phase 2t
       phase_barrier();
       softmax_phase(t);  // phase 2t + 1
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<kInFlight>());
       phase_barrier();
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
+      if constexpr (kStages == 2)
+        if (t < n_tiles) fetch_tile(t, t);
       softmax_phase(t - 1);  // phase 2t
       phase_barrier();
-      matrix_phase(t);  // phase 2t + 1; starts V_{t+1}
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
+      matrix_phase(t);  // phase 2t + 1
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<kInFlight>());
       phase_barrier();
     }
   }
