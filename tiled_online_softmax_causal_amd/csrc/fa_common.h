@@ -87,5 +87,24 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_dst) {
 #pragma clang diagnostic pop
 }
 
+// max(a, b, c) in one v_max3_f32 (the compiler forms it only sometimes).
+// Inputs are finite or -inf, never NaN.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// The same copy from base + voff: a wave-uniform 64-bit base (SGPRs) and a
+// 32-bit per-lane byte offset, so a lane keeps one VGPR per copy instead of a
+// 64-bit address.
+__device__ __forceinline__ void copy16_to_lds(const void* base, unsigned voff, char* lds_dst) {
+  const unsigned dst = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds_dst;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see the comment above
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(dst), "v"(voff), "s"(base) : "m0");
+#pragma clang diagnostic pop
+}
+
 }  // namespace common
 }  // namespace fa

@@ -23,14 +23,14 @@
 // barriers and per-phase bookkeeping per unit of work.
 //
 // Data movement.  Group 0 carries the K tiles and group 1 the V tiles, copied
-// HBM -> LDS directly (global_load_lds, no register staging) into rings of
-// kStages slots.  With BK = 64 (3 slots) K_{t+2} is started at the end of
-// group 0's matrix phase 2t and V_{t+1} at the end of group 1's matrix phase
-// 2t+1, three to four phases before their first reader.  With BK = 128 (2
-// slots, 128 KB of LDS for d = 128) K_{t+1} and V_t are started when phase 2t
-// begins, two phases before their first reader.  LDS rows are XOR-swizzled in
-// 16-byte chunks so the 128-bit K reads and the 64-bit transposed V reads are
-// free of bank conflicts on the 64-bank LDS.
+// HBM -> LDS directly (global_load_lds, no register staging) into a 3-slot K
+// ring and a 2-slot V ring (160 KB of LDS for d = 128 and 128-key tiles).  A
+// group issues its copies during its softmax phase, one between each pair of
+// exponential steps, so the copies trickle into the CU's memory pipeline
+// instead of arriving as one burst that would stall the issuing waves: K_{t+2}
+// in phase 2t+1 and V_t in phase 2t, two phases before their first reader.
+// LDS rows are XOR-swizzled in 16-byte chunks so the 128-bit K reads and the
+// 64-bit transposed V reads are free of bank conflicts on the 64-bank LDS.
 //
 // Register layout (v_mfma_f32_32x32x16_bf16).  Scores are formed transposed,
 // S^T = K . Q^T, so each lane owns ONE query (column lane%32) and half of the
@@ -43,15 +43,15 @@
 // core.
 //
 // Softmax.  Base 2: c = scale*log2(e) is folded into one FMA per score and exp
-// is v_exp_f32.  The maximum only guards exp2 against overflow, so it is
-// maintained lazily: the first tile sets it exactly, later tiles exponentiate
-// against the stale value at once, and only if some row's tile sum exceeds
-// 2^64 (a score at least ~59 above the stale maximum in base 2) is that tile
-// redone with the exact maximum and the accumulator and sum rescaled.  Since
-// numerator and denominator share the stale maximum, the result is unchanged;
-// probabilities below it underflow exactly as they would against the true one.
-// The denominator is an fp32 sum of the fp32 probabilities; only the P.V
-// operand is rounded to bf16.
+// is v_exp_f32.  The maximum only guards exp2 against overflow, so it is kept
+// with a bounded lag: every tile takes its row maximum, and the running
+// maximum (with the accumulator and sum rescaled) moves only when the tile's
+// exceeds it by more than 8 in base 2.  Probabilities thus stay below 2^8,
+// most tiles skip the rescale, and each fp32 score is dead once its
+// probability is formed.  Numerator and denominator share the running
+// maximum, so the result is that of the exact update up to rounding.  The
+// denominator is an fp32 sum of the fp32 probabilities; only the P.V operand
+// is rounded to bf16.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,7 +73,7 @@ constexpr int kGroupThreads = kThreads / 2;
 constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBQ = kQW * kWaves;       // query rows per workgroup
 constexpr int kAhead = 8;               // MFMAs between an operand's LDS read and its use
-constexpr float kOverflowSum = 0x1p64f; // a tile sum above this forces a rescale
+constexpr float kMaxSlack = 8.f;        // base-2 lag allowed between the running and true maxima
 
 // LDS tiles are row-major, D*2 bytes per row, with the 16-byte chunks of each
 // row XOR-swizzled by swz(row) (masked to the row's chunk count).  For d = 128
@@ -85,11 +85,12 @@ template <int D, int BK>
 struct Geo {
   static_assert(D == 64 || D == 128, "matrix-core path covers D = 64 and 128");
   static_assert(BK == 64 || BK == 128, "key tiles of 64 or 128 keys");
-  static constexpr int kStages = BK == 64 ? 3 : 2;               // depth of the K and V rings
+  static constexpr int kStagesK = 3;                            // depth of the K ring
+  static constexpr int kStagesV = 2;                            // depth of the V ring
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = kRowBytes / 16;               // 16-byte chunks per row
   static constexpr int kTileBytes = BK * kRowBytes;             // one K or V tile
-  static constexpr int kLdsBytes = 2 * kStages * kTileBytes;    // K ring, V ring
+  static constexpr int kLdsBytes = (kStagesK + kStagesV) * kTileBytes;
   static constexpr int kLoads = BK * kChunks / kGroupThreads;    // 16-byte loads per thread per tile
   static constexpr int kRowsPerLoad = kGroupThreads / kChunks;   // tile rows covered by one load step
   static_assert(BK * kChunks % kGroupThreads == 0, "a tile must split evenly over a 4-wave group");
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   constexpr int KB = BK / 32;  // 32-key blocks of S^T
   constexpr int KS = BK / 16;  // k-steps of the P.V MFMA
   constexpr int NL = G::kLoads;
-  constexpr int kStages = G::kStages;
+  static_assert(NL <= KS && KS % NL == 0, "copies are spread over the exponential steps");
 
   __shared__ __attribute__((aligned(16))) char lds[G::kLdsBytes];
 
@@ -168,10 +169,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   f32x16_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
+  // Scores and probabilities share registers: the bf16 probabilities of
+  // k-step ks (keys 16*ks.., 8 per lane) are written over the first four of
+  // the eight fp32 scores they come from, sacc[ks/2][8*(ks%2) + 0..3], and are
+  // read from there as the B operand of the P.V MFMA before the next score
+  // MFMAs overwrite the accumulator.
   f32x16_t sacc[KB];
-  bf16x8_t pb[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) pb[ks] = (bf16x8_t){};
+  for (int kb = 0; kb < KB; ++kb) sacc[kb] = (f32x16_t){};
+  auto p_operand = [&](int ks) {
+    const f32x16_t& a = sacc[ks >> 1];
+    const int r0 = 8 * (ks & 1);
+    const f32x4_t w = {a[r0], a[r0 + 1], a[r0 + 2], a[r0 + 3]};
+    return __builtin_bit_cast(bf16x8_t, w);
+  };
+  auto set_p = [&](int ks, bf16x8_t p8) {
+    const f32x4_t w = __builtin_bit_cast(f32x4_t, p8);
+    const int r0 = 8 * (ks & 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sacc[ks >> 1][r0 + j] = w[j];
+  };
   float m_run = -__builtin_inff(), l_run = 0.f;
 
   const int kv_end = CAUSAL ? min(S, q0 + kBQ) : S;
@@ -183,24 +200,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   // Thread gtid of the carrying group fills 16-byte slots gtid, gtid + 256, ...
   // (row-major) of its tensor's tile; the source is the logical chunk that the
   // swizzle puts in that slot.  Rows past the end of the sequence re-read row
-  // S-1 (their scores are masked).  Tile t lives in ring slot t % kStages.
+  // S-1 (their scores are masked).  K tile t lives in K slot t % 3, V tile t in
+  // V slot t % 2.
   const int gtid = tid & (kGroupThreads - 1);
   const int gwave = wave & 3;
   const int g_row = gtid / G::kChunks;
   const int g_lch = (gtid % G::kChunks) ^ swz<G::kChunks>(g_row);  // same for every load step
   const uint16_t* const src_g = (grp == 0 ? K : V) + head_off;
   char* const kbuf0 = lds;
-  char* const vbuf0 = lds + kStages * G::kTileBytes;
-  char* const ring_g = grp == 0 ? kbuf0 : vbuf0;
-  auto stage_of = [](int t) { return (t + kStages) % kStages; };
-  // Start the copy of tile t_src into the ring slot of tile t_dst (all load steps).
-  auto fetch_tile = [&](int t_src, int t_dst) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int grow = min(t_src * BK + g_row + i * G::kRowsPerLoad, S - 1);
-      copy16_to_lds(src_g + grow * D + g_lch * 8,
-                    ring_g + stage_of(t_dst) * G::kTileBytes + (i * kGroupThreads + gwave * 64) * 16);
-    }
+  char* const vbuf0 = lds + G::kStagesK * G::kTileBytes;
+  auto kslot = [](int t) { return (t + G::kStagesK) % G::kStagesK; };
+  auto vslot = [](int t) { return (t + G::kStagesV) % G::kStagesV; };
+  // load step i of the copy of tile t into this group's ring slot for t: a
+  // wave-uniform tile base and a 32-bit per-lane byte offset.  Rows clamp to
+  // S-1 (comparing whole offsets keeps the lane's chunk), and tiles past the
+  // last one re-read the last tile.
+  const unsigned g_off = (unsigned)(g_row * G::kRowBytes + g_lch * 16);
+  auto copy_step = [&](int i, int t, unsigned off0) {
+    const int t_src = min(t, n_tiles - 1);
+    const uint16_t* const tile = src_g + (size_t)t_src * BK * D;
+    const unsigned lim = (unsigned)((S - 1 - t_src * BK) * G::kRowBytes + g_lch * 16);
+    const unsigned voff = min(off0 + (unsigned)(i * G::kRowsPerLoad * G::kRowBytes), lim);
+    char* const slot = grp == 0 ? kbuf0 + kslot(t) * G::kTileBytes : vbuf0 + vslot(t) * G::kTileBytes;
+    copy16_to_lds(tile, voff, slot + (i * kGroupThreads + gwave * 64) * 16);
   };
   // per-lane read offsets within a tile.  K: row 32*kb + col, logical chunk
   // 2*ds + half.  V (transposed read): rows 16*ks + 4*half + u/4 (+8 for the
@@ -225,8 +247,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   auto matrix_body = [&](auto pv_c, auto sc_c, int t) {
     constexpr bool PV = decltype(pv_c)::value, SC = decltype(sc_c)::value;
     constexpr int NPV = PV ? DB * KS : 0, NSC = SC ? DS * KB : 0, N = NPV + NSC;
-    const char* Vl = vbuf0 + stage_of(t - 1) * G::kTileBytes;
-    const char* Kl = kbuf0 + stage_of(t) * G::kTileBytes;
+    // slot bases as opaque wave-uniform values: the compiler would otherwise
+    // strength-reduce t % 3 into one induction register per read address
+    const char* Vl = vbuf0 + __builtin_amdgcn_readfirstlane(vslot(t - 1) * G::kTileBytes);
+    const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(t) * G::kTileBytes);
     // the matrix-core wave issues first; the softmax wave on the same SIMD
     // fills the issue slots the MFMAs leave free
     __builtin_amdgcn_s_setprio(1);
@@ -239,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + v_off_hi[db]));
         const bf16x8_t av = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
                                                     __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p_operand(ks), oacc[db], 0, 0, 0);
       } else if (i < N) {
         const int j = i - NPV, ds = j / KB, kb = j % KB;
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
@@ -254,24 +278,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   // result is harmless: at t = 0 the probabilities are zero and the V ring slot
   // read was zero-filled, and once a wave is past its last tile (t > n_w) its
   // skipped softmax phases zero the probabilities, so the P.V product adds
-  // exactly 0; scores for t >= n_w are computed but never used.  With three
-  // ring slots, after its MFMAs are issued the wave starts its group's next
-  // tile copy: K_{t+2} (group 0) or V_{t+1} (group 1).  Past the last tile the
-  // copy re-reads the last tile into a slot nobody reads, which keeps the wait
-  // counts uniform.
-  auto matrix_phase = [&](int t) {
-    matrix_body(T_{}, T_{}, t);
-    if constexpr (kStages == 3) {
-      const int t_dst = grp == 0 ? t + 2 : t + 1;
-      fetch_tile(min(t_dst, n_tiles - 1), t_dst);
-    }
-  };
+  // exactly 0; scores for t >= n_w are computed but never used (at t = n_tiles
+  // from a K slot that may hold an older tile).
+  auto matrix_phase = [&](int t) { matrix_body(T_{}, T_{}, t); };
 
-  // ---- softmax phase t: S_t -> bf16 P_t, running max / sum
-  auto softmax_phase = [&](int t) {
+  // ---- softmax phase t: S_t -> bf16 P_t, running max / sum.  The NL load
+  // steps of the copy of tile t_copy are issued along the way, one per KS / NL
+  // exponential steps (pinned there by a scheduling barrier).
+  auto softmax_phase = [&](int t, int t_copy) {
+    // the copy offsets are formed here, not hoisted out of the loop, where
+    // they would hold registers through the matrix phase
+    unsigned off0 = g_off;
+    asm volatile("" : "+v"(off0));
+    auto copy_at = [&](int ks) {
+      if (ks % (KS / NL) == 0) {
+        copy_step(ks / (KS / NL), t_copy, off0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
     if (t < 0 || t >= n_w) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) pb[ks] = (bf16x8_t){};
+      for (int ks = 0; ks < KS; ++ks) {
+        set_p(ks, (bf16x8_t){});
+        copy_at(ks);
+      }
       return;
     }
     const int kv0 = t * BK;
@@ -290,66 +320,64 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           sacc[kb][r] = hidden ? -__builtin_inff() : sacc[kb][r] * c_log2;
         }
     }
-    // exponentiate against the running (possibly stale) maximum; all but the
-    // first tile try that directly and fall back to the exact update only when
-    // a probability could approach fp32 overflow
-    float rs = 0.f;
-    auto exponentiate = [&]() {
-      const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
-      rs = 0.f;
+    // The tile's row maximum (base 2).  The running maximum moves only when
+    // the tile's exceeds it by more than kMaxSlack, so probabilities stay
+    // below 2^kMaxSlack and the accumulator is rescaled only on those tiles
+    // (every row on its first visible tile).
+    float mxk[KB];  // one three-input max chain per 32-key block
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int kb = ks >> 1, r0 = 8 * (ks & 1);
-        bf16x8_t p8;
+    for (int kb = 0; kb < KB; ++kb) {
+      mxk[kb] = fmaxf(sacc[kb][0], sacc[kb][1]);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const f32x2_t x = {__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e], c_t, neg_m)),
-                             __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e + 1], c_t, neg_m))};
-          rs += x[0];
-          rs += x[1];
-          const bf16x2_t b = __builtin_convertvector(x, bf16x2_t);
-          p8[e] = b[0];
-          p8[e + 1] = b[1];
-        }
-        pb[ks] = p8;
-      }
-    };
-    bool exact = t == 0;
-    if (!exact) {
-      exponentiate();
-      exact = __builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0;
+      for (int r = 2; r < 16; r += 2) mxk[kb] = max3(mxk[kb], sacc[kb][r], sacc[kb][r + 1]);
     }
-    if (exact) {
-      float mx = -__builtin_inff();
+    float mx = mxk[0];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
-      const float m_new = fmaxf(m_run, max_halves(mx) * c_t);
+    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mxk[kb]);
+    const float m_tile = max_halves(mx) * c_t;
+    const bool moves = m_tile > m_run + kMaxSlack;
+    if (__builtin_amdgcn_ballot_w64(moves) != 0) {
+      const float m_new = moves ? m_tile : m_run;
       const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       m_run = m_new;
-      exponentiate();
+    }
+    // exponentiate against the running maximum, the copies interleaved
+    const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kb = ks >> 1, r0 = 8 * (ks & 1);
+      bf16x8_t p8;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const f32x2_t x = {__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e], c_t, neg_m)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e + 1], c_t, neg_m))};
+        rs += x[0];
+        rs += x[1];
+        const bf16x2_t b = __builtin_convertvector(x, bf16x2_t);
+        p8[e] = b[0];
+        p8[e + 1] = b[1];
+      }
+      set_p(ks, p8);
+      copy_at(ks);
     }
     l_run += rs;
   };
 
-  // ---- prologue: group 0 starts K_0 (and, with three slots, K_1); group 1
-  // zero-fills the V ring slot that the first matrix phase reads with zero
-  // probabilities (and, with three slots, starts V_0)
+  // ---- prologue: group 0 copies K_0 and K_1 and waits for K_0; group 1
+  // zero-fills the V slot that the first matrix phase reads with zero
+  // probabilities
   if (grp == 0) {
-    fetch_tile(0, 0);
-    if constexpr (kStages == 3) {
-      fetch_tile(min(1, n_tiles - 1), 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
-    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) copy_step(i, 0, g_off);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) copy_step(i, 1, g_off);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
   } else {
-    if constexpr (kStages == 3) fetch_tile(0, 0);
-    char* v_prev = vbuf0 + stage_of(-1) * G::kTileBytes;
+    char* v_prev = vbuf0 + vslot(-1) * G::kTileBytes;
     for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
       *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the zeros are in LDS
@@ -358,34 +386,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
 
   // ---- 2 * (n_tiles + 1) phases, one barrier each.  The two groups run the
   // same phases with their roles swapped; each has its own straight loop.
-  // Three slots: group 0 starts K_{t+2} at the end of phase 2t, group 1
-  // starts V_{t+1} at the end of phase 2t+1, and before the barrier that
-  // closes phase 2t+1 each group waits until only its latest copy is in
-  // flight.  Two slots: K_{t+1} (group 0) and V_t (group 1) start when phase
-  // 2t begins, into the slots last read in phase 2t-1, and have landed at the
-  // barrier that closes phase 2t+1.  Either way K_{t+1} and V_t are in LDS
-  // before their first reader, phase 2t+2, and a ring slot is refilled only
-  // after the phase that last reads its previous tile.  (Past the last tile a
-  // K copy re-reads the last tile into a slot that holds only junk scores.)
-  constexpr int kInFlight = kStages == 3 ? NL : 0;
+  // Group 0 copies K_{t+2} during phase 2t+1 into the slot last read in phase
+  // 2t-1 and, before the barrier closing phase 2t+1, waits for K_{t+1} (its
+  // copy from phase 2t-1).  Group 1 copies V_t during phase 2t into the slot
+  // last read in phase 2t-1 and waits for it before the barrier closing phase
+  // 2t+1.  So K_{t+1} and V_t are in LDS before their first reader, phase
+  // 2t+2.  Past the last tile the copies re-read the last tile into slots
+  // that hold nothing still needed, which keeps the wait counts uniform.
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
-      if constexpr (kStages == 2)
-        if (t < n_tiles) fetch_tile(min(t + 1, n_tiles - 1), t + 1);
       matrix_phase(t);  // phase 2t
       phase_barrier();
-      softmax_phase(t);  // phase 2t + 1
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<kInFlight>());
+      softmax_phase(t, t + 2);  // phase 2t + 1
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
       phase_barrier();
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
-      if constexpr (kStages == 2)
-        if (t < n_tiles) fetch_tile(t, t);
-      softmax_phase(t - 1);  // phase 2t
+      softmax_phase(t - 1, t);  // phase 2t
       phase_barrier();
       matrix_phase(t);  // phase 2t + 1
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<kInFlight>());
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
       phase_barrier();
     }
   }
