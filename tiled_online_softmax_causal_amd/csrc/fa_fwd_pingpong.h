@@ -43,15 +43,16 @@
 // core.
 //
 // Softmax.  Base 2: c = scale*log2(e) is folded into one FMA per score and exp
-// is v_exp_f32.  The maximum only guards exp2 against overflow, so it is kept
-// with a bounded lag: every tile takes its row maximum, and the running
-// maximum (with the accumulator and sum rescaled) moves only when the tile's
-// exceeds it by more than 8 in base 2.  Probabilities thus stay below 2^8,
-// most tiles skip the rescale, and each fp32 score is dead once its
-// probability is formed.  Numerator and denominator share the running
-// maximum, so the result is that of the exact update up to rounding.  The
-// denominator is an fp32 sum of the fp32 probabilities; only the P.V operand
-// is rounded to bf16.
+// is v_exp_f32.  The maximum only guards exp2 against overflow, so it is
+// maintained lazily: the first tile sets it exactly, later tiles exponentiate
+// against the running value at once, and only if some row's tile sum passes
+// 2^64 is the tile redone with the exact maximum (its scores recomputed from
+// the K tile still in LDS) and the accumulator and sum rescaled.  Numerator
+// and denominator share the running maximum, so the result is that of the
+// exact update up to rounding; probabilities below it underflow as they
+// would against the true one.  The bf16 probabilities are written over the
+// fp32 scores they come from.  The denominator is an fp32 sum of the fp32
+// probabilities; only the P.V operand is rounded to bf16.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,7 +74,7 @@ constexpr int kGroupThreads = kThreads / 2;
 constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBQ = kQW * kWaves;       // query rows per workgroup
 constexpr int kAhead = 8;               // MFMAs between an operand's LDS read and its use
-constexpr float kMaxSlack = 8.f;        // base-2 lag allowed between the running and true maxima
+constexpr float kOverflowSum = 0x1p64f; // a tile sum above this redoes the tile with the exact maximum
 
 // LDS tiles are row-major, D*2 bytes per row, with the 16-byte chunks of each
 // row XOR-swizzled by swz(row) (masked to the row's chunk count).  For d = 128
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     int xcd_group) {
   using G = Geo<D, BK>;
   using T_ = std::true_type;
+  using F_ = std::false_type;
   constexpr int DS = D / 16;   // k-steps of the score MFMA
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   constexpr int KB = BK / 32;  // 32-key blocks of S^T
@@ -306,11 +308,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     }
     const int kv0 = t * BK;
     const int qi = q0w + col;
-    float c_t = c_log2;
     // Tiles that straddle the diagonal or run past S move to the base-2 domain
     // here, so a hidden score is a plain -inf even when the scale is 0.
-    if ((CAUSAL && kv0 + BK - 1 > q0w) || kv0 + BK > S) {
-      c_t = 1.f;
+    const bool masked = (CAUSAL && kv0 + BK - 1 > q0w) || kv0 + BK > S;
+    const float c_t = masked ? 1.f : c_log2;
+    auto apply_mask = [&]() {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -319,50 +321,73 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           const bool hidden = (CAUSAL && kj > qi) || kj >= S;
           sacc[kb][r] = hidden ? -__builtin_inff() : sacc[kb][r] * c_log2;
         }
-    }
-    // The tile's row maximum (base 2).  The running maximum moves only when
-    // the tile's exceeds it by more than kMaxSlack, so probabilities stay
-    // below 2^kMaxSlack and the accumulator is rescaled only on those tiles
-    // (every row on its first visible tile).
-    float mxk[KB];  // one three-input max chain per 32-key block
+    };
+    if (masked) apply_mask();
+    // exponentiate against the running maximum (the copies interleaved when
+    // COPIES); rs is the lane's share of the tile's row sum
+    float rs = 0.f;
+    auto exponentiate = [&](auto copies_c) {
+      constexpr bool COPIES = decltype(copies_c)::value;
+      const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
+      rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      mxk[kb] = fmaxf(sacc[kb][0], sacc[kb][1]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int kb = ks >> 1, r0 = 8 * (ks & 1);
+        bf16x8_t p8;
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) mxk[kb] = max3(mxk[kb], sacc[kb][r], sacc[kb][r + 1]);
-    }
-    float mx = mxk[0];
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2_t x = {__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e], c_t, neg_m)),
+                             __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e + 1], c_t, neg_m))};
+          rs += x[0];
+          rs += x[1];
+          const bf16x2_t b = __builtin_convertvector(x, bf16x2_t);
+          p8[e] = b[0];
+          p8[e + 1] = b[1];
+        }
+        set_p(ks, p8);
+        if constexpr (COPIES) copy_at(ks);
+      }
+    };
+    // The first tile sets the running maximum exactly (its copies go out in
+    // one burst, once per workgroup).  Later tiles exponentiate against it at
+    // once; only if some row's tile sum then passes 2^64 (a score about 58
+    // above the running maximum, base 2) is the tile redone: its scores, which
+    // the probabilities have overwritten, are recomputed from K_t (still in
+    // its LDS slot: K_{t+3} is copied two phases later), the maximum is taken
+    // exactly, and O and l are rescaled.
+    auto take_exact_max = [&]() {
+      float mxk[KB];  // one three-input max chain per 32-key block
 #pragma unroll
-    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mxk[kb]);
-    const float m_tile = max_halves(mx) * c_t;
-    const bool moves = m_tile > m_run + kMaxSlack;
-    if (__builtin_amdgcn_ballot_w64(moves) != 0) {
-      const float m_new = moves ? m_tile : m_run;
+      for (int kb = 0; kb < KB; ++kb) {
+        mxk[kb] = fmaxf(sacc[kb][0], sacc[kb][1]);
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) mxk[kb] = max3(mxk[kb], sacc[kb][r], sacc[kb][r + 1]);
+      }
+      float mx = mxk[0];
+#pragma unroll
+      for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mxk[kb]);
+      const float m_new = fmaxf(m_run, max_halves(mx) * c_t);
       const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       m_run = m_new;
-    }
-    // exponentiate against the running maximum, the copies interleaved
-    const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
-    float rs = 0.f;
+    };
+    if (t == 0) take_exact_max();
+    exponentiate(T_{});
+    if (t > 0 && __builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
+      const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(t) * G::kTileBytes);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int kb = ks >> 1, r0 = 8 * (ks & 1);
-      bf16x8_t p8;
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const f32x2_t x = {__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e], c_t, neg_m)),
-                           __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e + 1], c_t, neg_m))};
-        rs += x[0];
-        rs += x[1];
-        const bf16x2_t b = __builtin_convertvector(x, bf16x2_t);
-        p8[e] = b[0];
-        p8[e + 1] = b[1];
-      }
-      set_p(ks, p8);
-      copy_at(ks);
+        for (int ds = 0; ds < DS; ++ds) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      if (masked) apply_mask();
+      take_exact_max();
+      exponentiate(F_{});
     }
     l_run += rs;
   };
