@@ -107,6 +107,40 @@ int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype d
  * one (batch, head) of length S (0 for an unsupported variant).  Host-only. */
 int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant);
 
+/*
+ * fa_dense_fwd -- the dense, materialising forward pass on the GPU: the
+ * standard attention of the aiml.sh page "Speed up long contexts with
+ * FlashAttention" (lab.py, standard_attention), whose N x N score and
+ * probability matrices the page's traffic model (run-output.txt,
+ * hbm_traffic_sweep) charges to HBM.  It computes the same O and lse as
+ * fa_fwd, in three kernels: S = scale * Q K^T (fp32, to the workspace),
+ * P = softmax(S) per row (normalised, bf16, to the workspace; lse from the
+ * row's maximum and sum), O = P V.  Under the causal rule only the 128 x 128
+ * tiles at or below the diagonal are computed, written and read.  It is the
+ * baseline against which the tiled path's traffic and time are measured.
+ *
+ *   q, k, v, o, lse, B, H, S, causal, scale, stream: as for fa_fwd
+ *   D          64 or 128
+ *   dtype      FA_DTYPE_BF16 only
+ *   workspace  device memory owned by the caller, 16-byte aligned, at least
+ *              fa_dense_workspace_bytes(S) bytes (one head).  The (batch,
+ *              head) pairs are processed in chunks of as many heads as fit:
+ *              workspace_bytes / fa_dense_workspace_bytes(S).  Its contents
+ *              on return are unspecified; calls that share a workspace must
+ *              be ordered on one stream.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT (also for a NULL, misaligned or
+ * too small workspace), FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_dense_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale,
+                       fa_dtype dtype, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_dense_fwd needs per (batch, head): S rows of the fp32
+ * score matrix and S rows of the bf16 probability matrix, each row padded to
+ * a multiple of 8 elements; 0 for S < 1.  Host-only. */
+int64_t fa_dense_workspace_bytes(int64_t S);
+
 /* Static, never-NULL description of a status code. */
 const char *fa_status_str(fa_status status);
 

@@ -112,3 +112,32 @@ def test_scheduler_tile_counts(S, causal):
 def test_scheduler_page_worked_example():
     """16x16 blocks over 64 rows visit 10 tiles (run-output.txt, flash_tiles_visited)."""
     assert causal_kv_tiles(64, 16, 16) == 10
+
+
+# ---------------------------------------------------------------- the dense, materialising entry point
+
+def test_dense_workspace_bytes():
+    """fp32 scores + bf16 probabilities, S rows each, rows padded to 8 elements."""
+    assert fa.dense_workspace_bytes(0) == 0
+    assert fa.dense_workspace_bytes(1) == 8 * 1 * 6
+    assert fa.dense_workspace_bytes(1000) == 1000 * 1000 * 6
+    assert fa.dense_workspace_bytes(1001) == 1008 * 1001 * 6
+    assert fa.dense_workspace_bytes(8192) == 8192 * 8192 * 6
+
+
+def _dense(ws=P, ws_bytes=1 << 40, dtype=fa.FA_DTYPE_BF16, D=128, ptrs=(P, P, P, P), B=1, H=1, S=64,
+           scale=0.1):
+    return fa.fa_dense_fwd_raw(*ptrs, 0, B, H, S, D, True, scale, dtype, ws, ws_bytes)
+
+
+def test_dense_rejects_before_launch():
+    per_head = fa.dense_workspace_bytes(64)
+    assert _dense(ws=0) == fa.FA_ERR_INVALID_ARGUMENT                      # no workspace
+    assert _dense(ws_bytes=per_head - 1) == fa.FA_ERR_INVALID_ARGUMENT     # smaller than one head
+    assert _dense(ws=P + 8) == fa.FA_ERR_INVALID_ARGUMENT                  # misaligned workspace
+    assert _dense(ptrs=(P, P, 0, P)) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _dense(B=0) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _dense(scale=float("nan")) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _dense(dtype=fa.FA_DTYPE_FP32) == fa.FA_ERR_UNSUPPORTED         # bf16 only
+    assert _dense(D=32) == fa.FA_ERR_UNSUPPORTED                           # D 64 or 128
+    assert _dense(dtype=7) == fa.FA_ERR_UNSUPPORTED

@@ -23,7 +23,8 @@ VARIANTS = {"auto": 0, "mfma_b256": 1, "mfma_b128": 2, "valu": 3, "mfma_b256_k12
 
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_fwd_select_variant", "fa_fwd_tiles_per_head",
-           "fa_status_str", "fa_last_hip_error", "fa_version")
+           "fa_dense_fwd", "fa_dense_workspace_bytes", "fa_status_str", "fa_last_hip_error",
+           "fa_version")
 
 _lib = None
 
@@ -51,6 +52,10 @@ def load_library(path: str = LIBRARY_PATH):
     lib.fa_fwd_select_variant.restype = i32
     lib.fa_fwd_tiles_per_head.argtypes = [i64, i32, i32]
     lib.fa_fwd_tiles_per_head.restype = i64
+    lib.fa_dense_fwd.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, p, i64, p]
+    lib.fa_dense_fwd.restype = i32
+    lib.fa_dense_workspace_bytes.argtypes = [i64]
+    lib.fa_dense_workspace_bytes.restype = i64
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -158,3 +163,56 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
                             dtype, st, variant)
     _check(status)
     return (out, lse) if return_lse else out
+
+
+def dense_workspace_bytes(S: int) -> int:
+    """Workspace bytes fa_dense_fwd needs per (batch, head) at sequence length S."""
+    return load_library().fa_dense_workspace_bytes(S)
+
+
+def fa_dense_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                     S: int, D: int, causal: bool, scale: float, dtype: int, ws_ptr: int,
+                     ws_bytes: int, stream: int = 0) -> int:
+    """Call fa_dense_fwd with raw device addresses; returns the fa_status code."""
+    lib = load_library()
+    return lib.fa_dense_fwd(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None,
+                            lse_ptr or None, B, H, S, D, int(bool(causal)), float(scale), dtype,
+                            ws_ptr or None, int(ws_bytes), stream or None)
+
+
+def dense_fwd(q, k, v, causal: bool = True, scale: float | None = None, workspace=None,
+              max_workspace_bytes: int | None = None, stream=None):
+    """The dense, materialising forward on ``[B, H, S, D]`` bf16 CUDA tensors.
+
+    Returns ``(o, lse)`` like :func:`fwd`.  ``workspace`` is a uint8 CUDA tensor
+    of at least :func:`dense_workspace_bytes` bytes; without one, a workspace
+    for all heads (or ``max_workspace_bytes``, rounded down to whole heads) is
+    allocated here, the library itself allocates nothing.
+    """
+    import torch
+
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise ValueError("q, k, v must be bf16 device tensors")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    per_head = dense_workspace_bytes(S)
+    if workspace is None:
+        n = B * H if max_workspace_bytes is None else max(1, min(B * H, max_workspace_bytes // per_head))
+        workspace = torch.empty(n * per_head, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        status = fa_dense_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr(), B, H, S, D, causal, scale, FA_DTYPE_BF16,
+                                  workspace.data_ptr(), workspace.numel(), st)
+    _check(status)
+    return out, lse

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "fa_dense.h"
 #include "fa_fwd_pingpong.h"
 #include "fa_mfma_bf16.h"
 #include "fa_valu.h"
@@ -127,6 +128,24 @@ hipError_t launch_valu_d(const void* q, const void* k, const void* v, void* o, f
   }
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_dense(const void* q, const void* k, const void* v, void* o, float* lse, int64_t nb, int64_t S,
+                        float scale, float* smat, uint16_t* pmat, hipStream_t stream) {
+  namespace dn = fa::dense;
+  const int n_qt = (int)ceil_div(S, dn::kTile);
+  const int64_t pitch = dn::pitch_of(S);
+  const int64_t n_pairs = CAUSAL ? (int64_t)n_qt * (n_qt + 1) / 2 : (int64_t)n_qt * n_qt;
+  hipLaunchKernelGGL((dn::dense_scores<D, CAUSAL>), dim3((unsigned)(nb * n_pairs)), dim3(dn::kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), smat, (int)S, n_qt, pitch,
+                     scale);
+  const int64_t n_rows = nb * S;
+  hipLaunchKernelGGL((dn::dense_softmax<CAUSAL>), dim3((unsigned)ceil_div(n_rows, dn::kThreads / 64)),
+                     dim3(dn::kThreads), 0, stream, smat, pmat, lse, (int)S, pitch, n_rows);
+  hipLaunchKernelGGL((dn::dense_pv<D, CAUSAL>), dim3((unsigned)(nb * n_qt)), dim3(dn::kThreads), 0, stream, pmat,
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), (int)S, n_qt, pitch);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,6 +219,59 @@ fa_status fa_fwd_variant(const void* q, const void* k, const void* v, void* o, f
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                  int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, void* stream) {
   return fa_fwd_variant(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, FA_VARIANT_AUTO, stream);
+}
+
+int64_t fa_dense_workspace_bytes(int64_t S) { return S < 1 ? 0 : fa::dense::head_bytes(S); }
+
+fa_status fa_dense_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                       int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  namespace dn = fa::dense;
+  if (!q || !k || !v || !o || !workspace) return FA_ERR_INVALID_ARGUMENT;
+  if (B < 1 || H < 1 || S < 1 || D < 1) return FA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 16))
+    return FA_ERR_INVALID_ARGUMENT;
+  if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARGUMENT;
+  if (dtype != FA_DTYPE_BF16 || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  if (S * D >= (int64_t(1) << 31) || B > INT32_MAX / H) return FA_ERR_UNSUPPORTED;
+  const int64_t per_head = dn::head_bytes(S);
+  if (workspace_bytes < per_head) return FA_ERR_INVALID_ARGUMENT;
+  const int64_t BH = B * H;
+  const int64_t n_qt = ceil_div(S, dn::kTile);
+  const int64_t n_pairs = causal ? n_qt * (n_qt + 1) / 2 : n_qt * n_qt;
+  // heads per chunk: what the workspace holds, within a one-dimensional grid
+  int64_t nb = workspace_bytes / per_head;
+  nb = nb < BH ? nb : BH;
+  const int64_t grid_cap = INT32_MAX / (n_pairs > 4 ? n_pairs : 4);
+  nb = nb < grid_cap ? nb : grid_cap;
+  if (nb < 1) return FA_ERR_UNSUPPORTED;
+  const int64_t pitch = dn::pitch_of(S);
+  float* smat = static_cast<float*>(workspace);
+  uint16_t* pmat = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + nb * S * pitch * 4);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t head_elems = S * D;
+  for (int64_t h0 = 0; h0 < BH; h0 += nb) {
+    const int64_t n = BH - h0 < nb ? BH - h0 : nb;
+    const auto* qh = static_cast<const uint16_t*>(q) + h0 * head_elems;
+    const auto* kh = static_cast<const uint16_t*>(k) + h0 * head_elems;
+    const auto* vh = static_cast<const uint16_t*>(v) + h0 * head_elems;
+    auto* oh = static_cast<uint16_t*>(o) + h0 * head_elems;
+    float* lh = lse ? lse + h0 * S : nullptr;
+    hipError_t err;
+    if (D == 128)
+      err = causal ? launch_dense<128, true>(qh, kh, vh, oh, lh, n, S, scale, smat, pmat, st)
+                   : launch_dense<128, false>(qh, kh, vh, oh, lh, n, S, scale, smat, pmat, st);
+    else
+      err = causal ? launch_dense<64, true>(qh, kh, vh, oh, lh, n, S, scale, smat, pmat, st)
+                   : launch_dense<64, false>(qh, kh, vh, oh, lh, n, S, scale, smat, pmat, st);
+    if (err != hipSuccess) {
+      g_last_hip_error = static_cast<int>(err);
+      return FA_ERR_HIP;
+    }
+  }
+  return FA_OK;
 }
 
 const char* fa_status_str(fa_status status) {
