@@ -1,0 +1,47 @@
+"""Host logic of the tiled-vs-dense comparison: rocprofv3 counter files -> HBM bytes per call.
+
+Synthetic counter files: a 1 GiB device copy whose FETCH_SIZE reads 0.5 GiB and
+whose WRITE_SIZE reads 1 GiB (so the scale factors are 2 and 1, as measured on
+gfx950), and one call of each path with known counter values.
+"""
+import csv
+
+from tiled_online_softmax_causal_amd.compare import traffic
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, counter, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_counters_scaled_by_copy_calibration(tmp_path):
+    kib = 1024 * 1024  # KiB in 1 GiB
+    _write(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", kib / 2)] * 3 +
+           [("vectorized_elementwise_kernel<FillFunctor>", "FETCH_SIZE", 123.0)])
+    _write(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", kib)] * 3)
+    _write(tmp_path / "f.csv", [
+        ("distribution_elementwise_grid_stride_kernel", "FETCH_SIZE", 999.0),  # input generation: ignored
+        ("void fa::pp::attn_fwd_pingpong<128, 128, true>(...)", "FETCH_SIZE", 100.0),
+        ("void fa::dense::dense_scores<128, true>(...)", "FETCH_SIZE", 10.0),
+        ("void fa::dense::dense_softmax<true>(...)", "FETCH_SIZE", 20.0),
+        ("void fa::dense::dense_pv<128, true>(...)", "FETCH_SIZE", 30.0)])
+    _write(tmp_path / "w.csv", [
+        ("void fa::pp::attn_fwd_pingpong<128, 128, true>(...)", "WRITE_SIZE", 7.0),
+        ("void fa::dense::dense_scores<128, true>(...)", "WRITE_SIZE", 40.0),
+        ("void fa::dense::dense_pv<128, true>(...)", "WRITE_SIZE", 2.0)])
+    out = traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                  str(tmp_path / "cw.csv"), calls=1)
+    assert out["fetch_factor"] == 2.0 and out["write_factor"] == 1.0
+    assert out["flash"] == {"read_bytes": 100 * 1024 * 2, "write_bytes": 7 * 1024, "total_bytes": 207 * 1024,
+                            "dispatches_per_call": 1.0}
+    assert out["dense"]["read_bytes"] == 60 * 1024 * 2
+    assert out["dense"]["write_bytes"] == 42 * 1024
+    assert out["dense"]["dispatches_per_call"] == 3.0
+    halved = traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                     str(tmp_path / "cw.csv"), calls=2)
+    assert halved["dense"]["total_bytes"] == out["dense"]["total_bytes"] // 2

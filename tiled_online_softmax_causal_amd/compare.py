@@ -1,0 +1,153 @@
+"""Measured comparison of the tiled and the dense attention forward on one MI355X.
+
+    python -m tiled_online_softmax_causal_amd.compare [--seq 1024,4096,16384,32768]
+        [--batch 1] [--heads 32] [--dim 128] [--paths flash,dense] [--steps 5] [--warmup 2]
+    python -m tiled_online_softmax_causal_amd.compare --traffic FETCH.csv WRITE.csv \\
+        COPY_FETCH.csv COPY_WRITE.csv --calls N
+
+The first form times both GPU paths -- fa_fwd (tiled, online softmax) and
+fa_dense_fwd (score and probability matrices through HBM) -- at each sequence
+length on seeded uniform(-0.8, 0.8) bf16 inputs, causal, and prints one JSON
+line per (S, path) with the measured time, TFLOP/s, effective GB/s of the
+compulsory bytes, and the logical bytes of the aiml.sh page's model
+(run-output.txt, hbm_traffic_sweep: b1 h32 d128, S = 1024 ... 32768) for the
+same shape.  The second form turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+counter files of such a run into measured HBM bytes per call of each path,
+scaled by the counters of a plain device copy of known size
+(bench.py --copy-calibration).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import math
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+
+
+def _path_of(kernel_name: str):
+    if "attn_fwd" in kernel_name:
+        return "flash"
+    if "dense_" in kernel_name:
+        return "dense"
+    return None
+
+
+def _counter_kib(path: str) -> dict:
+    """Sum of a counter (KiB) over each path's dispatches, and the dispatch counts."""
+    tot, n = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = _path_of(r["Kernel_Name"])
+            if key is None:
+                continue
+            tot[key] = tot.get(key, 0.0) + float(r["Counter_Value"])
+            n[key] = n.get(key, 0) + 1
+    return {k: (tot[k], n[k]) for k in tot}
+
+
+def _copy_kib(path: str) -> float:
+    """Mean of a counter (KiB) over the plain device copies (rocclr copyBuffer)."""
+    with open(path) as f:
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(f) if "copyBuffer" in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no copy dispatches in {path}")
+    return sum(vals) / len(vals)
+
+
+def traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str, calls: int,
+            copy_mib: int = 1024) -> dict:
+    """HBM bytes per call of each path, each counter scaled by its plain-copy reading."""
+    f_fac = copy_mib * 1024 / _copy_kib(copy_fetch_csv)
+    w_fac = copy_mib * 1024 / _copy_kib(copy_write_csv)
+    fetch, write = _counter_kib(fetch_csv), _counter_kib(write_csv)
+    out = {"fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)}
+    for p in sorted(set(fetch) | set(write)):
+        rd = fetch.get(p, (0.0, 0))[0] * 1024 * f_fac / calls
+        wr = write.get(p, (0.0, 0))[0] * 1024 * w_fac / calls
+        out[p] = {"read_bytes": int(rd), "write_bytes": int(wr), "total_bytes": int(rd + wr),
+                  "dispatches_per_call": fetch.get(p, (0, 0))[1] / calls}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--seq", default="1024,4096,16384,32768")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--heads", type=int, default=32)
+    ap.add_argument("--dim", type=int, default=128)
+    ap.add_argument("--paths", default="flash,dense")
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--max-workspace-gib", type=float, default=64.0,
+                    help="workspace of the dense path; heads are processed in chunks that fit")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
+    ap.add_argument("--calls", type=int, default=1, help="attention calls per path in the profiled run")
+    args = ap.parse_args()
+    if args.traffic:
+        print(json.dumps(traffic(*args.traffic, calls=args.calls)))
+        return
+
+    import torch
+
+    import tiled_online_softmax_causal_amd as fa
+    from tiled_online_softmax_causal_amd.costmodel import algorithmic_bytes, attention_flops, page_logical_traffic
+    from workloads import uniform_qkv_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, D = args.batch, args.heads, args.dim
+    paths = args.paths.split(",")
+    for S in (int(s) for s in args.seq.split(",")):
+        q, k, v = uniform_qkv_device(B, H, S, D, seed=42, dtype=torch.bfloat16, device=dev)
+        scale = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32).item())
+        model = page_logical_traffic(S, num_heads=B * H, head_dim=D)
+        for path in paths:
+            ws = None
+            if path == "dense":
+                per_head = fa.dense_workspace_bytes(S)
+                n = max(1, min(B * H, int(args.max_workspace_gib * 2**30) // per_head))
+                ws = torch.empty(n * per_head, dtype=torch.uint8, device=dev)
+
+            def call():
+                if path == "dense":
+                    return fa.dense_fwd(q, k, v, causal=True, scale=scale, workspace=ws)
+                return fa.fwd(q, k, v, causal=True, scale=scale)
+
+            for _ in range(args.warmup):
+                call()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for _ in range(args.steps):
+                call()
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / args.steps
+            flops = attention_flops(B, H, S, D, True)
+            nbytes = algorithmic_bytes(B, H, S, D, 2)
+            print(json.dumps({
+                "path": path, "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
+                "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                "compulsory_bytes": nbytes, "effective_gbs": round(nbytes / ms / 1e6, 1),
+                "dense_workspace_heads": None if ws is None else ws.numel() // fa.dense_workspace_bytes(S),
+                "page_model_mb": {"standard_total": round(model["standard_total_bytes"] / 1e6, 2),
+                                  "tiled_logical": round(model["tiled_logical_bytes"] / 1e6, 2),
+                                  "qkvo_compulsory": round(model["qkvo_bytes"] / 1e6, 2)},
+            }), flush=True)
+            del ws
+            torch.cuda.empty_cache()
+        del q, k, v
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()
