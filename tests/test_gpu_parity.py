@@ -217,6 +217,22 @@ def test_b1_h32_s32768_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("B,H,S", [(1, 5, 16384), (2, 8, 5000)])
+def test_resident_grid_sequences(B, H, S):
+    """More work items than CUs, so one resident workgroup per CU walks a sequence of
+    items: h5 (heads not grouped per XCD, items taken in strides of the grid) and
+    b2 h8 S5000 (grouped per XCD, 40 items per XCD for 32 workgroups: a partial
+    second round).  Sampled rows of every head."""
+    case(f"bf16 {B}x{H}x{S}x128 causal, resident grid")
+    q, k, v = device_inputs(B, H, S, 128, seed=S)
+    o, lse = run_fwd(q, k, v)
+    rows = sample_rows(S, 24, tile_edges=(128, 256))
+    bh = list(range(B * H))
+    ref_o, ref_l = oracle_on(q, k, v, True, scale_of(128), bh_idx=bh, row_idx=rows)
+    og, lg = gather(o, lse, bh, rows)
+    assert_close(og, lg, ref_o, ref_l, torch.bfloat16, f"resident {B}x{H}x{S}")
+
+
 # ---------------------------------------------------------------- closed forms at full size
 
 @pytest.mark.parametrize("shape", [(8, 32, 8192, 128), (1, 32, 32768, 128), (2, 3, 1000, 64)])

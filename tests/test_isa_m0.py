@@ -60,7 +60,8 @@ def test_m0_is_only_the_lds_copy_destination(device_asm):
         for k, ins in enumerate(body):
             assert not M0_READERS.search(ins), f"{name}: unexpected M0 reader: {ins}"
             if re.search(r"\bm0\b", ins):
-                assert re.match(r"s_mov_b32 m0, s\d+$", ins), f"{name}: M0 written by: {ins}"
+                # the LDS address, from whatever scalar register holds it
+                assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", ins), f"{name}: M0 written by: {ins}"
                 assert body[k + 1].startswith("global_load_lds_dwordx4"), f"{name}: M0 write not followed by a copy"
             if ins.startswith("global_load_lds_dwordx4"):
-                assert re.match(r"s_mov_b32 m0, s\d+$", body[k - 1]), f"{name}: copy without its M0 write"
+                assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", body[k - 1]), f"{name}: copy without its M0 write"

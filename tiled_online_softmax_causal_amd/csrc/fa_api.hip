@@ -77,11 +77,29 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* o, flo
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// The ping-pong kernel holds a whole CU (LDS), so with more work items than
+// CUs it runs resident: one workgroup per CU walking its items, instead of a
+// grid of one workgroup per item that the dispatcher refills as they finish.
 template <int D, int BK>
 hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
                            int64_t S, int causal, float scale, hipStream_t stream) {
   const int64_t n_qb = ceil_div(S, fa::pp::kBQ);
-  const int64_t grid = BH * n_qb;
+  const int64_t n_items = BH * n_qb;
+  const int cus = device_cus();
+  const int64_t grid = cus >= 8 && n_items > cus ? cus : n_items;
   const int xcd_group = (BH % kNumXcd) == 0;
   const float c = std::fabs(scale) * kLog2e;
   const int negate_q = scale < 0.f;
@@ -91,10 +109,10 @@ hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o,
   auto* O = static_cast<uint16_t*>(o);
   if (causal)
     hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
-                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, c, negate_q, xcd_group);
+                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)n_items, c, negate_q, xcd_group);
   else
     hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
-                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, c, negate_q, xcd_group);
+                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)n_items, c, negate_q, xcd_group);
   return hipGetLastError();
 }
 

@@ -71,6 +71,37 @@ __device__ __forceinline__ void schedule_block(int wg, int n_qb, int xcd_group, 
   }
 }
 
+// The k-th work item (bh, query block) of workgroup w in a grid of G
+// workgroups over n_items = (heads) x n_qb items; false once w has none left.
+// With one item per workgroup (G >= n_items) this is schedule_block.  With
+// fewer, resident workgroups (one per CU), each walks a static sequence:
+// when heads are grouped per XCD (G a multiple of 8), the P = G/8 workgroups
+// of an XCD take the XCD's items P at a time in the heaviest-first order, the
+// order reversed every other round ("snake"), so that over two rounds every
+// workgroup gets about the same work and the workgroups of an XCD stay on
+// the same or adjacent heads, sharing their K/V in that XCD's L2.
+__device__ __forceinline__ bool next_item(int w, int k, int G, int n_qb, int n_items, int xcd_group, int& bh,
+                                          int& qb) {
+  if (G >= n_items) {
+    if (k > 0) return false;
+    schedule_block(w, n_qb, xcd_group, bh, qb);
+    return true;
+  }
+  if (xcd_group && (G & 7) == 0) {
+    const int P = G >> 3, xcd = w & 7, j = w >> 3;
+    const int idx = P * k + ((k & 1) ? P - 1 - j : j);
+    if (idx >= (n_items >> 3)) return false;
+    bh = (idx / n_qb) * 8 + xcd;
+    qb = n_qb - 1 - idx % n_qb;
+    return true;
+  }
+  const int item = w + G * k;
+  if (item >= n_items) return false;
+  bh = item / n_qb;
+  qb = n_qb - 1 - item % n_qb;
+  return true;
+}
+
 // Start one 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane
 // l's 16 bytes land at lds_dst + 16*l (lds_dst is wave-uniform).  Issued from
 // inline assembly so that the compiler does not track it: it would otherwise

@@ -126,8 +126,8 @@ __device__ __forceinline__ void schedule_matrix_phase(std::integer_sequence<int,
 template <int D, int BK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int S, int n_qb, float c_log2, int negate_q,
-    int xcd_group) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int S, int n_qb, int n_items, float c_log2,
+    int negate_q, int xcd_group) {
   using G = Geo<D, BK>;
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -148,8 +148,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   const int half = lane >> 5;  // which key half of each 32-key block
   const int u = lane & 15, quad = lane >> 4;
 
+  // one work item (bh, query block) per iteration; a grid of one workgroup per
+  // item runs one iteration each, a resident grid walks its sequence
+  for (int item = 0;; ++item) {
   int bh, qb;
-  schedule_block(blockIdx.x, n_qb, xcd_group, bh, qb);
+  if (!next_item(blockIdx.x, item, gridDim.x, n_qb, n_items, xcd_group, bh, qb)) break;
   const size_t head_off = (size_t)bh * S * D;
   const uint16_t* Qh = Q + head_off;
   const int q0 = qb * kBQ;
@@ -454,6 +457,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       }
     if (LSE && half == 0) LSE[(size_t)bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
   }
+  }  // next work item: every wave has passed the last phase barrier, so the
+     // next prologue may overwrite the rings
 }
 
 }  // namespace pp
