@@ -33,7 +33,10 @@ def device_asm(tmp_path_factory):
 
 
 def _kernels(asm: str):
-    """(name, instruction lines) for every kernel body in the assembly."""
+    """(name, instruction lines) for every kernel body in the assembly.
+
+    A body runs from the kernel's label to its .Lfunc_end label, so kernels with
+    several exits (s_endpgm) are read whole."""
     out, name, body = [], None, []
     for line in asm.splitlines():
         m = re.match(r"^(_Z\w+):", line)
@@ -42,12 +45,13 @@ def _kernels(asm: str):
             continue
         if name is None:
             continue
+        if line.startswith(".Lfunc_end"):
+            out.append((name, body))
+            name = None
+            continue
         text = line.split(";")[0].strip()
         if text and not text.startswith("."):
             body.append(text)
-        if text.startswith("s_endpgm"):
-            out.append((name, body))
-            name = None
     return out
 
 

@@ -148,11 +148,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   const int half = lane >> 5;  // which key half of each 32-key block
   const int u = lane & 15, quad = lane >> 4;
 
-  // one work item (bh, query block) per iteration; a grid of one workgroup per
-  // item runs one iteration each, a resident grid walks its sequence
-  for (int item = 0;; ++item) {
+  // One work item (bh, query block) per iteration; a grid of one workgroup per
+  // item runs one iteration each, a resident grid walks its sequence.  The K
+  // and V rings keep one tile numbering across items (offsets offK, offV), so
+  // the last copies of an item bring in the next item's first tiles.
+  int offK = 0, offV = 0;
   int bh, qb;
-  if (!next_item(blockIdx.x, item, gridDim.x, n_qb, n_items, xcd_group, bh, qb)) break;
+  if (!next_item(blockIdx.x, 0, gridDim.x, n_qb, n_items, xcd_group, bh, qb)) return;
+  for (int item = 0;; ++item) {
+  int bh_n = 0, qb_n = 0;
+  const bool have_next = next_item(blockIdx.x, item + 1, gridDim.x, n_qb, n_items, xcd_group, bh_n, qb_n);
   const size_t head_off = (size_t)bh * S * D;
   const uint16_t* Qh = Q + head_off;
   const int q0 = qb * kBQ;
@@ -200,34 +205,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   const int n_tiles = (kv_end + BK - 1) / BK;
   // tiles this wave takes part in (its rows see keys below min(S, q0w + 32))
   const int n_w = q0w >= S ? 0 : (CAUSAL ? min(n_tiles, (min(q0w + kQW, S) - 1) / BK + 1) : n_tiles);
+  const int kv_end_n = CAUSAL ? min(S, qb_n * kBQ + kBQ) : S;  // the next item's key range
+  const int n_tiles_n = (kv_end_n + BK - 1) / BK;
 
   // ---- staging: HBM -> LDS directly (global_load_lds, 16 bytes per lane).
   // Thread gtid of the carrying group fills 16-byte slots gtid, gtid + 256, ...
   // (row-major) of its tensor's tile; the source is the logical chunk that the
   // swizzle puts in that slot.  Rows past the end of the sequence re-read row
-  // S-1 (their scores are masked).  K tile t lives in K slot t % 3, V tile t in
-  // V slot t % 2.
+  // S-1 (their scores are masked).  K tile t lives in K slot (t + offK) % 3,
+  // V tile t in V slot (t + offV) % 2.
   const int gtid = tid & (kGroupThreads - 1);
   const int gwave = wave & 3;
   const int g_row = gtid / G::kChunks;
   const int g_lch = (gtid % G::kChunks) ^ swz<G::kChunks>(g_row);  // same for every load step
   const uint16_t* const src_g = (grp == 0 ? K : V) + head_off;
+  const uint16_t* const src_n = (grp == 0 ? K : V) + (size_t)bh_n * S * D;
   char* const kbuf0 = lds;
   char* const vbuf0 = lds + G::kStagesK * G::kTileBytes;
-  auto kslot = [](int t) { return (t + G::kStagesK) % G::kStagesK; };
-  auto vslot = [](int t) { return (t + G::kStagesV) % G::kStagesV; };
-  // load step i of the copy of tile t into this group's ring slot for t: a
-  // wave-uniform tile base and a 32-bit per-lane byte offset.  Rows clamp to
-  // S-1 (comparing whole offsets keeps the lane's chunk), and tiles past the
-  // last one re-read the last tile.
+  auto kslot = [&](int t) { return (t + offK + G::kStagesK) % G::kStagesK; };
+  auto vslot = [&](int t) { return (t + offV + G::kStagesV) % G::kStagesV; };
+  // One tile copy: source tile (wave-uniform base), its rows left before the
+  // end of the sequence, and the ring slot.  A null tile means no copy.
+  struct Copy {
+    const uint16_t* tile;
+    int rows;
+    char* slot;
+  };
+  // The copy into this group's ring position td: this item's tile td (clamped
+  // to its last tile; group 0's K positions run to n_tiles, one past the last
+  // tile, for the unused scores of the final matrix phase), then the next
+  // item's first tiles, or with no next item the last tile again.
+  auto copy_for = [&](int td) -> Copy {
+    char* const slot = grp == 0 ? kbuf0 + kslot(td) * G::kTileBytes : vbuf0 + vslot(td) * G::kTileBytes;
+    const int n_self = grp == 0 ? n_tiles + 1 : n_tiles;
+    int ts;
+    const uint16_t* base;
+    if (td < n_self || !have_next) {
+      ts = min(td, n_tiles - 1);
+      base = src_g;
+    } else {
+      ts = min(td - n_self, n_tiles_n - 1);
+      base = src_n;
+    }
+    return Copy{base + (size_t)ts * BK * D, S - ts * BK, slot};
+  };
+  // load step i of a copy: a 32-bit per-lane byte offset from the tile base;
+  // rows clamp to the sequence's last row (comparing whole offsets keeps the
+  // lane's chunk)
   const unsigned g_off = (unsigned)(g_row * G::kRowBytes + g_lch * 16);
-  auto copy_step = [&](int i, int t, unsigned off0) {
-    const int t_src = min(t, n_tiles - 1);
-    const uint16_t* const tile = src_g + (size_t)t_src * BK * D;
-    const unsigned lim = (unsigned)((S - 1 - t_src * BK) * G::kRowBytes + g_lch * 16);
+  auto copy_step = [&](int i, const Copy& c, unsigned off0) {
+    const unsigned lim = (unsigned)((c.rows - 1) * G::kRowBytes + g_lch * 16);
     const unsigned voff = min(off0 + (unsigned)(i * G::kRowsPerLoad * G::kRowBytes), lim);
-    char* const slot = grp == 0 ? kbuf0 + kslot(t) * G::kTileBytes : vbuf0 + vslot(t) * G::kTileBytes;
-    copy16_to_lds(tile, voff, slot + (i * kGroupThreads + gwave * 64) * 16);
+    copy16_to_lds(c.tile, voff, c.slot + (i * kGroupThreads + gwave * 64) * 16);
   };
   // per-lane read offsets within a tile.  K: row 32*kb + col, logical chunk
   // 2*ds + half.  V (transposed read): rows 16*ks + 4*half + u/4 (+8 for the
@@ -288,25 +317,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   auto matrix_phase = [&](int t) { matrix_body(T_{}, T_{}, t); };
 
   // ---- softmax phase t: S_t -> bf16 P_t, running max / sum.  The NL load
-  // steps of the copy of tile t_copy are issued along the way, one per KS / NL
-  // exponential steps (pinned there by a scheduling barrier).
-  auto softmax_phase = [&](int t, int t_copy) {
+  // steps of copy cp are issued along the way, one per KS / NL exponential
+  // steps (pinned there by a scheduling barrier).
+  auto softmax_phase = [&](int t, const Copy& cp) {
     // the copy offsets are formed here, not hoisted out of the loop, where
     // they would hold registers through the matrix phase
     unsigned off0 = g_off;
     asm volatile("" : "+v"(off0));
     auto copy_at = [&](int ks) {
       if (ks % (KS / NL) == 0) {
-        copy_step(ks / (KS / NL), t_copy, off0);
+        copy_step(ks / (KS / NL), cp, off0);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (t < 0 || t >= n_w) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        set_p(ks, (bf16x8_t){});
-        copy_at(ks);
-      }
+      for (int ks = 0; ks < KS; ++ks) set_p(ks, (bf16x8_t){});
+      if (cp.tile)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) copy_at(ks);
       return;
     }
     const int kv0 = t * BK;
@@ -395,51 +424,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     l_run += rs;
   };
 
-  // ---- prologue: group 0 copies K_0 and K_1 and waits for K_0; group 1
-  // zero-fills the V slot that the first matrix phase reads with zero
-  // probabilities
-  if (grp == 0) {
+  // ---- prologue of the first item: group 0 copies K_0 and K_1 and waits for
+  // K_0; group 1 copies V_0 and zero-fills the V slot that the first matrix
+  // phase reads with zero probabilities.  Later items find K_0, K_1 and V_0
+  // already copied by the previous item (waited for before its last barrier
+  // and K_1 in flight, as within an item), and their first matrix phase reads
+  // the previous item's last V tile (finite) with zero probabilities.
+  if (item == 0) {
+    if (grp == 0) {
+      const Copy k0 = copy_for(0), k1 = copy_for(1);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) copy_step(i, 0, g_off);
+      for (int i = 0; i < NL; ++i) copy_step(i, k0, g_off);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) copy_step(i, 1, g_off);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
-  } else {
-    char* v_prev = vbuf0 + vslot(-1) * G::kTileBytes;
-    for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
-      *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the zeros are in LDS
+      for (int i = 0; i < NL; ++i) copy_step(i, k1, g_off);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
+    } else {
+      const Copy v0 = copy_for(0);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) copy_step(i, v0, g_off);
+      char* v_prev = vbuf0 + vslot(-1) * G::kTileBytes;
+      for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
+        *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the zeros are in LDS
+    }
+    phase_barrier();
   }
-  phase_barrier();
 
   // ---- 2 * (n_tiles + 1) phases, one barrier each.  The two groups run the
   // same phases with their roles swapped; each has its own straight loop.
-  // Group 0 copies K_{t+2} during phase 2t+1 into the slot last read in phase
-  // 2t-1 and, before the barrier closing phase 2t+1, waits for K_{t+1} (its
-  // copy from phase 2t-1).  Group 1 copies V_t during phase 2t into the slot
-  // last read in phase 2t-1 and waits for it before the barrier closing phase
-  // 2t+1.  So K_{t+1} and V_t are in LDS before their first reader, phase
-  // 2t+2.  Past the last tile the copies re-read the last tile into slots
-  // that hold nothing still needed, which keeps the wait counts uniform.
+  // Group 0 copies ring position t+2 during phase 2t+1 into the slot last read
+  // in phase 2t-1 and, before the barrier closing phase 2t+1, waits for
+  // position t+1 (its copy from phase 2t-1).  Group 1 copies position t during
+  // phase 2t (t >= 1) into the slot last read in phase 2t-1 and waits for it
+  // before the barrier closing phase 2t+1.  So K_{t+1} and V_t are in LDS
+  // before their first reader, phase 2t+2.  The copies past this item's tiles
+  // are the next item's first tiles.
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
       matrix_phase(t);  // phase 2t
       phase_barrier();
-      softmax_phase(t, t + 2);  // phase 2t + 1
+      softmax_phase(t, copy_for(t + 2));  // phase 2t + 1
       __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
       phase_barrier();
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
-      softmax_phase(t - 1, t);  // phase 2t
+      softmax_phase(t - 1, t == 0 ? Copy{nullptr, 0, nullptr} : copy_for(t));  // phase 2t
       phase_barrier();
       matrix_phase(t);  // phase 2t + 1
       __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
       phase_barrier();
     }
   }
-  // no global->LDS copy may still be writing when the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), lse = ln2 * (m + log2 l)
   const int qi = q0w + col;
@@ -457,8 +493,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       }
     if (LSE && half == 0) LSE[(size_t)bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
   }
-  }  // next work item: every wave has passed the last phase barrier, so the
-     // next prologue may overwrite the rings
+  offK = (offK + n_tiles + 1) % G::kStagesK;
+  offV = (offV + n_tiles) % G::kStagesV;
+  if (!have_next) break;
+  bh = bh_n;
+  qb = qb_n;
+  }
+  // no global->LDS copy may still be writing when the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
 }
 
 }  // namespace pp
