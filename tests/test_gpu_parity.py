@@ -233,6 +233,29 @@ def test_resident_grid_sequences(B, H, S):
     assert_close(og, lg, ref_o, ref_l, torch.bfloat16, f"resident {B}x{H}x{S}")
 
 
+@pytest.mark.parametrize("B,H,S,D,causal,scale", [
+    (4, 80, 100, 128, True, None),     # one-tile items: a K copy runs two items ahead
+    (4, 80, 129, 64, True, None),      # two-tile items, the second one key wide
+    (1, 10, 8000, 128, False, None),   # non-causal: every item sees all 63 tiles
+    (1, 5, 16384, 128, True, -0.05),   # negative scale across item boundaries
+    (2, 8, 5000, 64, True, None),      # d = 64
+])
+def test_resident_grid_edge_items(B, H, S, D, causal, scale):
+    """Resident grids (more items than CUs) at the edges of the item chaining: the tile
+    sequence of a workgroup runs across item boundaries, where one matrix phase
+    finishes an item and starts the next.  Sampled rows of every head (all rows for
+    the short sequences)."""
+    scale = scale_of(D) if scale is None else scale
+    case(f"bf16 {B}x{H}x{S}x{D} causal={causal} scale={scale}, resident grid")
+    q, k, v = device_inputs(B, H, S, D, seed=S + D)
+    o, lse = run_fwd(q, k, v, causal=causal, scale=scale)
+    rows = np.arange(S) if S <= 256 else sample_rows(S, 16, tile_edges=(128, 256))
+    bh = list(range(B * H))
+    ref_o, ref_l = oracle_on(q, k, v, causal, scale, bh_idx=bh, row_idx=rows)
+    og, lg = gather(o, lse, bh, rows)
+    assert_close(og, lg, ref_o, ref_l, torch.bfloat16, f"resident edge {B}x{H}x{S}x{D}")
+
+
 # ---------------------------------------------------------------- closed forms at full size
 
 @pytest.mark.parametrize("shape", [(8, 32, 8192, 128), (1, 32, 32768, 128), (2, 3, 1000, 64)])

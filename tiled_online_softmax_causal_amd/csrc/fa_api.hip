@@ -101,18 +101,17 @@ hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o,
   const int cus = device_cus();
   const int64_t grid = cus >= 8 && n_items > cus ? cus : n_items;
   const int xcd_group = (BH % kNumXcd) == 0;
-  const float c = std::fabs(scale) * kLog2e;
-  const int negate_q = scale < 0.f;
+  const float c = scale * kLog2e;  // the kernel takes a scale of either sign
   const auto* Q = static_cast<const uint16_t*>(q);
   const auto* K = static_cast<const uint16_t*>(k);
   const auto* V = static_cast<const uint16_t*>(v);
   auto* O = static_cast<uint16_t*>(o);
   if (causal)
     hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
-                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)n_items, c, negate_q, xcd_group);
+                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)n_items, c, xcd_group);
   else
     hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
-                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)n_items, c, negate_q, xcd_group);
+                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)n_items, c, xcd_group);
   return hipGetLastError();
 }
 

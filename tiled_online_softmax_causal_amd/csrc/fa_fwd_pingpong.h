@@ -7,28 +7,38 @@
 // Key blocks wholly above the diagonal are never visited; blocks that straddle
 // it are masked per element.  This kernel is that loop laid out for CDNA4.
 //
-// Work split.  A workgroup owns 256 query rows of one (batch, head) and runs 8
-// waves of 32 rows each, two waves per SIMD.  Waves 0-3 (group 0) and 4-7
-// (group 1) alternate between two kinds of phase, one phase apart:
+// Work split.  A work item is 256 query rows of one (batch, head); a
+// workgroup runs 8 waves of 32 rows each, two waves per SIMD.  With more items
+// than CUs the grid is one workgroup per CU, each walking a list of items, and
+// the key tiles of its items, item after item, form one tile sequence
+// T = 0 .. N-1 that the phases run through without a break.  Waves 0-3
+// (group 0) and 4-7 (group 1) alternate between two kinds of phase, one phase
+// apart:
 //
-//     phase 2t     group 0: matrix phase t      group 1: softmax phase t-1
-//     phase 2t+1   group 0: softmax phase t     group 1: matrix phase t
+//     phase 2T     group 0: matrix phase T      group 1: softmax of tile T-1
+//     phase 2T+1   group 0: softmax of tile T   group 1: matrix phase T
 //
-// where the matrix phase t issues O^T += V_{t-1}^T P_{t-1}^T and then
-// S_t^T = K_t Q^T on the matrix cores (32 MFMAs per 64 keys for d = 128) and
-// the softmax phase t turns S_t into bf16 probabilities on the vector ALUs.
+// where the matrix phase T issues O^T += V_{T-1}^T P_{T-1}^T and then
+// S_T^T = K_T Q^T on the matrix cores (32 MFMAs per 64 keys for d = 128) and
+// the softmax of tile T turns S_T into bf16 probabilities on the vector ALUs.
 // Every SIMD thus holds one wave feeding its matrix core and one wave doing the
 // exponentials, the two kinds of work overlap, and one workgroup barrier closes
-// each phase.  A key tile is BK = 64 or 128 keys; the longer tile halves the
-// barriers and per-phase bookkeeping per unit of work.
+// each phase.  At an item boundary one matrix phase finishes an item (its last
+// P.V product) and starts the next (its first scores); the softmax of an
+// item's first tile writes out the previous item before its own work, and the
+// softmax of an item's last tile loads the next item's Q.  A key tile is
+// BK = 64 or 128 keys; the longer tile halves the barriers and per-phase
+// bookkeeping per unit of work.
 //
 // Data movement.  Group 0 carries the K tiles and group 1 the V tiles, copied
 // HBM -> LDS directly (global_load_lds, no register staging) into a 3-slot K
 // ring and a 2-slot V ring (160 KB of LDS for d = 128 and 128-key tiles).  A
 // group issues its copies during its softmax phase, one between each pair of
 // exponential steps, so the copies trickle into the CU's memory pipeline
-// instead of arriving as one burst that would stall the issuing waves: K_{t+2}
-// in phase 2t+1 and V_t in phase 2t, two phases before their first reader.
+// instead of arriving as one burst that would stall the issuing waves: K_{T+2}
+// in phase 2T+1 and V_T in phase 2T, two phases before their first reader.
+// The rings number tiles along the sequence, so the last copies of an item
+// bring in the next item's first tiles.
 // LDS rows are XOR-swizzled in 16-byte chunks so the 128-bit K reads and the
 // 64-bit transposed V reads are free of bank conflicts on the 64-bank LDS.
 //
@@ -38,12 +48,12 @@
 // and row sum are lane-local plus one v_permlane32_swap.  The fp32 scores,
 // exponentiated and packed to bf16, are already the B operand of
 // O^T = V^T . P^T; V^T comes from LDS through ds_read_b64_tr_b16 in the
-// matching key order.  The MFMA operands read from LDS run eight MFMAs ahead
+// matching key order.  The MFMA operands read from LDS run five MFMAs ahead
 // of their use (a pinned issue order), so LDS latency hides behind the matrix
 // core.
 //
-// Softmax.  Base 2: c = scale*log2(e) is folded into one FMA per score and exp
-// is v_exp_f32.  The maximum only guards exp2 against overflow, so it is
+// Softmax.  Base 2: c = scale*log2(e) (of either sign) is folded into one FMA
+// per score and exp is v_exp_f32.  The maximum only guards exp2 against overflow, so it is
 // maintained lazily: the first tile sets it exactly, later tiles exponentiate
 // against the running value at once, and only if some row's tile sum passes
 // 2^64 is the tile redone with the exact maximum (its scores recomputed from
@@ -73,7 +83,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupThreads = kThreads / 2;
 constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBQ = kQW * kWaves;       // query rows per workgroup
-constexpr int kAhead = 8;               // MFMAs between an operand's LDS read and its use
+constexpr int kAhead = 5;               // MFMAs between an operand's LDS read and its use
 constexpr float kOverflowSum = 0x1p64f; // a tile sum above this redoes the tile with the exact maximum
 
 // LDS tiles are row-major, D*2 bytes per row, with the 16-byte chunks of each
@@ -127,7 +137,7 @@ template <int D, int BK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int S, int n_qb, int n_items, float c_log2,
-    int negate_q, int xcd_group) {
+    int xcd_group) {
   using G = Geo<D, BK>;
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -148,33 +158,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   const int half = lane >> 5;  // which key half of each 32-key block
   const int u = lane & 15, quad = lane >> 4;
 
-  // One work item (bh, query block) per iteration; a grid of one workgroup per
-  // item runs one iteration each, a resident grid walks its sequence.  The K
-  // and V rings keep one tile numbering across items (offsets offK, offV), so
-  // the last copies of an item bring in the next item's first tiles.
-  int offK = 0, offV = 0;
-  int bh, qb;
-  if (!next_item(blockIdx.x, 0, gridDim.x, n_qb, n_items, xcd_group, bh, qb)) return;
-  for (int item = 0;; ++item) {
-  int bh_n = 0, qb_n = 0;
-  const bool have_next = next_item(blockIdx.x, item + 1, gridDim.x, n_qb, n_items, xcd_group, bh_n, qb_n);
-  const size_t head_off = (size_t)bh * S * D;
-  const uint16_t* Qh = Q + head_off;
-  const int q0 = qb * kBQ;
-  const int q0w = q0 + wave * kQW;
+  // ---- work items and the flattened tile sequence.  The workgroup walks its
+  // items (bh, query block) in order (one item when the grid has one
+  // workgroup per item); their key tiles, item after item, form one sequence
+  // T = 0 .. N-1 that the ping-pong pipeline runs without a break: the matrix
+  // phase that finishes an item (its last P.V product) also starts the next
+  // (its first scores), and the softmax phase of an item's first tile first
+  // writes out the previous item.  The K and V rings number tiles by T.
+  struct Item {
+    int bh, qb, n_tiles, k;
+    bool valid;
+  };
+  auto item_at = [&](int k) -> Item {
+    int b = 0, q = 0;
+    if (!next_item(blockIdx.x, k, gridDim.x, n_qb, n_items, xcd_group, b, q)) return Item{0, 0, 1, k, false};
+    const int kv_end = CAUSAL ? min(S, q * kBQ + kBQ) : S;
+    return Item{b, q, (kv_end + BK - 1) / BK, k, true};
+  };
+  Item cur = item_at(0);
+  if (!cur.valid) return;
+  int N = 0;
+  for (Item it = cur; it.valid; it = item_at(it.k + 1)) N += it.n_tiles;
 
-  // ---- Q^T operand: lane holds q[q0w + col][16*ds + 8*half + 0..7]
+  // ---- Q^T operand of an item: lane holds q[q0w + col][16*ds + 8*half + 0..7].
+  // Nothing but the score MFMAs reads it, so a load issued early in a phase
+  // is waited for only where those MFMAs need it.
   bf16x8_t qreg[DS];
-  {
-    const int qrow = min(q0w + col, S - 1);
-    const unsigned flip = negate_q ? 0x80008000u : 0u;
+  auto load_q = [&](const Item& it) {
+    const int qrow = min(it.qb * kBQ + wave * kQW + col, S - 1);
+    const uint16_t* src = Q + (size_t)it.bh * S * D + (size_t)qrow * D + 8 * half;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(Qh + (size_t)qrow * D + 16 * ds + 8 * half);
-      x ^= (u32x4_t){flip, flip, flip, flip};
-      qreg[ds] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
+    for (int ds = 0; ds < DS; ++ds) qreg[ds] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ds);
+  };
+  load_q(cur);
 
   f32x16_t oacc[DB];
 #pragma unroll
@@ -201,29 +217,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   };
   float m_run = -__builtin_inff(), l_run = 0.f;
 
-  const int kv_end = CAUSAL ? min(S, q0 + kBQ) : S;
-  const int n_tiles = (kv_end + BK - 1) / BK;
-  // tiles this wave takes part in (its rows see keys below min(S, q0w + 32))
-  const int n_w = q0w >= S ? 0 : (CAUSAL ? min(n_tiles, (min(q0w + kQW, S) - 1) / BK + 1) : n_tiles);
-  const int kv_end_n = CAUSAL ? min(S, qb_n * kBQ + kBQ) : S;  // the next item's key range
-  const int n_tiles_n = (kv_end_n + BK - 1) / BK;
-
   // ---- staging: HBM -> LDS directly (global_load_lds, 16 bytes per lane).
   // Thread gtid of the carrying group fills 16-byte slots gtid, gtid + 256, ...
   // (row-major) of its tensor's tile; the source is the logical chunk that the
   // swizzle puts in that slot.  Rows past the end of the sequence re-read row
-  // S-1 (their scores are masked).  K tile t lives in K slot (t + offK) % 3,
-  // V tile t in V slot (t + offV) % 2.
+  // S-1 (their scores are masked).  K tile T lives in K slot T % 3, V tile T
+  // in V slot T % 2.
   const int gtid = tid & (kGroupThreads - 1);
   const int gwave = wave & 3;
   const int g_row = gtid / G::kChunks;
   const int g_lch = (gtid % G::kChunks) ^ swz<G::kChunks>(g_row);  // same for every load step
-  const uint16_t* const src_g = (grp == 0 ? K : V) + head_off;
-  const uint16_t* const src_n = (grp == 0 ? K : V) + (size_t)bh_n * S * D;
   char* const kbuf0 = lds;
   char* const vbuf0 = lds + G::kStagesK * G::kTileBytes;
-  auto kslot = [&](int t) { return (t + offK + G::kStagesK) % G::kStagesK; };
-  auto vslot = [&](int t) { return (t + offV + G::kStagesV) % G::kStagesV; };
+  auto kslot = [](int T) { return (T + G::kStagesK) % G::kStagesK; };
+  auto vslot = [](int T) { return (T + G::kStagesV) % G::kStagesV; };
   // One tile copy: source tile (wave-uniform base), its rows left before the
   // end of the sequence, and the ring slot.  A null tile means no copy.
   struct Copy {
@@ -231,23 +238,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     int rows;
     char* slot;
   };
-  // The copy into this group's ring position td: this item's tile td (clamped
-  // to its last tile; group 0's K positions run to n_tiles, one past the last
-  // tile, for the unused scores of the final matrix phase), then the next
-  // item's first tiles, or with no next item the last tile again.
-  auto copy_for = [&](int td) -> Copy {
-    char* const slot = grp == 0 ? kbuf0 + kslot(td) * G::kTileBytes : vbuf0 + vslot(td) * G::kTileBytes;
-    const int n_self = grp == 0 ? n_tiles + 1 : n_tiles;
-    int ts;
-    const uint16_t* base;
-    if (td < n_self || !have_next) {
-      ts = min(td, n_tiles - 1);
-      base = src_g;
+  // The copy cursor walks this group's tensor along the tile sequence; past
+  // its end it keeps re-reading the last tile into the next slots, which keeps
+  // the wait counts uniform.
+  Item c_it = cur;
+  int c_t = 0, c_T = 0;
+  auto next_copy = [&]() -> Copy {
+    const Copy c{(grp == 0 ? K : V) + (size_t)c_it.bh * S * D + (size_t)c_t * BK * D, S - c_t * BK,
+                 grp == 0 ? kbuf0 + kslot(c_T) * G::kTileBytes : vbuf0 + vslot(c_T) * G::kTileBytes};
+    ++c_T;
+    if (c_t + 1 < c_it.n_tiles) {
+      ++c_t;
     } else {
-      ts = min(td - n_self, n_tiles_n - 1);
-      base = src_n;
+      const Item nx = item_at(c_it.k + 1);
+      if (nx.valid) {
+        c_it = nx;
+        c_t = 0;
+      }
     }
-    return Copy{base + (size_t)ts * BK * D, S - ts * BK, slot};
+    return c;
   };
   // load step i of a copy: a 32-bit per-lane byte offset from the tile base;
   // rows clamp to the sequence's last row (comparing whole offsets keeps the
@@ -276,20 +285,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     }
   }
 
-  // ---- matrix phase t: O^T += V_{t-1}^T P_{t-1}^T (DB accumulators, k-step
-  // outer), then S_t^T = K_t Q^T (KB accumulators, alternating).
-  auto matrix_body = [&](auto pv_c, auto sc_c, int t) {
-    constexpr bool PV = decltype(pv_c)::value, SC = decltype(sc_c)::value;
-    constexpr int NPV = PV ? DB * KS : 0, NSC = SC ? DS * KB : 0, N = NPV + NSC;
+  // ---- matrix phase T: O^T += V_{T-1}^T P_{T-1}^T (DB accumulators, k-step
+  // outer), then S_T^T = K_T Q^T (KB accumulators, alternating).
+  auto matrix_phase = [&](int T) {
+    constexpr int NPV = DB * KS, NSC = DS * KB, NM = NPV + NSC;
     // slot bases as opaque wave-uniform values: the compiler would otherwise
-    // strength-reduce t % 3 into one induction register per read address
-    const char* Vl = vbuf0 + __builtin_amdgcn_readfirstlane(vslot(t - 1) * G::kTileBytes);
-    const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(t) * G::kTileBytes);
+    // strength-reduce T % 3 into one induction register per read address
+    const char* Vl = vbuf0 + __builtin_amdgcn_readfirstlane(vslot(T - 1) * G::kTileBytes);
+    const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(T) * G::kTileBytes);
     // the matrix-core wave issues first; the softmax wave on the same SIMD
     // fills the issue slots the MFMAs leave free
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < NM; ++i) {
       if (i < NPV) {
         const int ks = i / DB, db = i % DB;
         const char* vp = Vl + 16 * ks * G::kRowBytes;
@@ -298,28 +306,56 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
         const bf16x8_t av = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
                                                     __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p_operand(ks), oacc[db], 0, 0, 0);
-      } else if (i < N) {
+      } else {
         const int j = i - NPV, ds = j / KB, kb = j % KB;
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
       }
     }
-    if constexpr (N > 0) schedule_matrix_phase<NPV, N>(std::make_integer_sequence<int, N>{});
+    schedule_matrix_phase<NPV, NM>(std::make_integer_sequence<int, NM>{});
     __builtin_amdgcn_s_setprio(0);
   };
-  // Every wave runs the same full body in every matrix phase, which keeps the
-  // loop's register allocation simple.  Where a product is not needed its
-  // result is harmless: at t = 0 the probabilities are zero and the V ring slot
-  // read was zero-filled, and once a wave is past its last tile (t > n_w) its
-  // skipped softmax phases zero the probabilities, so the P.V product adds
-  // exactly 0; scores for t >= n_w are computed but never used (at t = n_tiles
-  // from a K slot that may hold an older tile).
-  auto matrix_phase = [&](int t) { matrix_body(T_{}, T_{}, t); };
+  // Every matrix phase runs the same full body, which keeps the loop's
+  // register allocation simple.  Where a product is not needed its result is
+  // harmless: in phase 0 the probabilities are zero and the V ring slot read
+  // was zero-filled, and for a tile a wave does not see (past its rows'
+  // diagonal) its softmax phase zeroes the probabilities, so the P.V product
+  // adds exactly 0; the scores of phase N (past the last tile) are never used.
 
-  // ---- softmax phase t: S_t -> bf16 P_t, running max / sum.  The NL load
-  // steps of copy cp are issued along the way, one per KS / NL exponential
-  // steps (pinned there by a scheduling barrier).
-  auto softmax_phase = [&](int t, const Copy& cp) {
+  // ---- epilogue of an item: O = acc / l (bf16, round to nearest even),
+  // lse = ln2 * (m + log2 l); then the state starts over for the next item
+  auto finish_item = [&](const Item& it) {
+    const int qi = it.qb * kBQ + wave * kQW + col;
+    const float l_tot = sum_halves(l_run);
+    if (qi < S) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = O + (size_t)it.bh * S * D + (size_t)qi * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4_t v4 = {oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv,
+                              oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv};
+          *reinterpret_cast<bf16x4_t*>(orow + 32 * db + 8 * rg + 4 * half) = __builtin_convertvector(v4, bf16x4_t);
+        }
+      if (LSE && half == 0) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
+    m_run = -__builtin_inff();
+    l_run = 0.f;
+  };
+
+  // ---- softmax phase for tile t of item `it` (flattened index T): S -> bf16
+  // P, running max / sum.  The NL load steps of copy cp are issued along the
+  // way, one per KS / NL exponential steps (pinned there by a scheduling
+  // barrier).  When `next_q` is set the next item's Q operand has already been
+  // loaded over this item's (its latency hidden by this phase), and the rare
+  // recompute below reloads this item's first.
+  auto softmax_phase = [&](const Item& it, int t, int T, const Copy& cp, bool next_q, const Item& nx) {
+    const int q0w = it.qb * kBQ + wave * kQW;
+    // tiles this wave takes part in (its rows see keys below min(S, q0w + 32))
+    const int n_w = q0w >= S ? 0 : (CAUSAL ? min(it.n_tiles, (min(q0w + kQW, S) - 1) / BK + 1) : it.n_tiles);
     // the copy offsets are formed here, not hoisted out of the loop, where
     // they would hold registers through the matrix phase
     unsigned off0 = g_off;
@@ -330,12 +366,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (t < 0 || t >= n_w) {
+    if (t >= n_w) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) set_p(ks, (bf16x8_t){});
-      if (cp.tile)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) copy_at(ks);
+      for (int ks = 0; ks < KS; ++ks) copy_at(ks);
       return;
     }
     const int kv0 = t * BK;
@@ -380,25 +415,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
         if constexpr (COPIES) copy_at(ks);
       }
     };
-    // The first tile sets the running maximum exactly (its copies go out in
-    // one burst, once per workgroup).  Later tiles exponentiate against it at
-    // once; only if some row's tile sum then passes 2^64 (a score about 58
-    // above the running maximum, base 2) is the tile redone: its scores, which
-    // the probabilities have overwritten, are recomputed from K_t (still in
-    // its LDS slot: K_{t+3} is copied two phases later), the maximum is taken
-    // exactly, and O and l are rescaled.
+    // The first tile sets the running maximum exactly.  Later tiles
+    // exponentiate against it at once; only if some row's tile sum then passes
+    // 2^64 (a score about 58 above the running maximum, base 2) is the tile
+    // redone: its scores, which the probabilities have overwritten, are
+    // recomputed from K_T (still in its LDS slot: K_{T+3} is copied two phases
+    // later), the maximum is taken exactly, and O and l are rescaled.
+    // (the maximum of the scaled scores: the scale may be negative)
     auto take_exact_max = [&]() {
       float mxk[KB];  // one three-input max chain per 32-key block
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        mxk[kb] = fmaxf(sacc[kb][0], sacc[kb][1]);
+        mxk[kb] = fmaxf(sacc[kb][0] * c_t, sacc[kb][1] * c_t);
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) mxk[kb] = max3(mxk[kb], sacc[kb][r], sacc[kb][r + 1]);
+        for (int r = 2; r < 16; r += 2) mxk[kb] = max3(mxk[kb], sacc[kb][r] * c_t, sacc[kb][r + 1] * c_t);
       }
       float mx = mxk[0];
 #pragma unroll
       for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mxk[kb]);
-      const float m_new = fmaxf(m_run, max_halves(mx) * c_t);
+      const float m_new = fmaxf(m_run, max_halves(mx));
       const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -408,15 +443,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     if (t == 0) take_exact_max();
     exponentiate(T_{});
     if (t > 0 && __builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
-      const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(t) * G::kTileBytes);
+      if (next_q) load_q(it);
+      const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(T) * G::kTileBytes);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_sched_barrier(0);  // one operand read at a time: this path is rare
         }
+      if (next_q) load_q(nx);
       if (masked) apply_mask();
       take_exact_max();
       exponentiate(F_{});
@@ -424,80 +461,85 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     l_run += rs;
   };
 
-  // ---- prologue of the first item: group 0 copies K_0 and K_1 and waits for
-  // K_0; group 1 copies V_0 and zero-fills the V slot that the first matrix
-  // phase reads with zero probabilities.  Later items find K_0, K_1 and V_0
-  // already copied by the previous item (waited for before its last barrier
-  // and K_1 in flight, as within an item), and their first matrix phase reads
-  // the previous item's last V tile (finite) with zero probabilities.
-  if (item == 0) {
-    if (grp == 0) {
-      const Copy k0 = copy_for(0), k1 = copy_for(1);
+  // ---- prologue: group 0 copies K_0 and K_1 and waits for K_0; group 1
+  // zero-fills the V slot that the first matrix phase reads with zero
+  // probabilities (V_0 is copied in phase 0)
+  if (grp == 0) {
+    const Copy k0 = next_copy(), k1 = next_copy();
 #pragma unroll
-      for (int i = 0; i < NL; ++i) copy_step(i, k0, g_off);
+    for (int i = 0; i < NL; ++i) copy_step(i, k0, g_off);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) copy_step(i, k1, g_off);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
-    } else {
-      const Copy v0 = copy_for(0);
+    for (int i = 0; i < NL; ++i) copy_step(i, k1, g_off);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
+  } else {
+    char* v_prev = vbuf0 + vslot(-1) * G::kTileBytes;
+    for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
+      *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the zeros are in LDS
+  }
+  phase_barrier();
+
+  // ---- 2 (N + 1) phases, one barrier each.  The two groups run the same
+  // phases with their roles swapped.  Group 0 copies K_{T+2} during phase
+  // 2T+1 into the slot last read in phase 2T-1 and, before the barrier
+  // closing phase 2T+1, waits for K_{T+1} (its copy from phase 2T-1).  Group 1
+  // copies V_T during phase 2T into the slot last read in phase 2T-1 and waits
+  // for it before the barrier closing phase 2T+1.  So K_{T+1} and V_T are in
+  // LDS before their first reader, phase 2T+2.  In the softmax phase of an
+  // item's first tile the previous item is written out first; in that of its
+  // last tile the next item's Q operand is loaded first.
+  Item prev = cur;
+  int T = 0;
+  // the softmax phase of tile t of the current item (flattened index T)
+  auto softmax_step = [&](int t, const Item& nx) {
+    const Copy cp = next_copy();
+    if (t == 0 && T > 0) finish_item(prev);
+    const bool next_q = t + 1 == cur.n_tiles && nx.valid;
+    if (next_q) load_q(nx);
+    softmax_phase(cur, t, T, cp, next_q, nx);
+  };
+  if (grp == 0) {
+    matrix_phase(0);  // phase 0
+    phase_barrier();
+    for (;;) {
+      const Item nx = item_at(cur.k + 1);
+      for (int t = 0; t < cur.n_tiles; ++t, ++T) {
+        softmax_step(t, nx);  // phase 2T + 1
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
+        phase_barrier();
+        matrix_phase(T + 1);  // phase 2T + 2
+        phase_barrier();
+      }
+      prev = cur;
+      if (!nx.valid) break;
+      cur = nx;
+    }
+    finish_item(prev);  // phase 2N + 1
+    phase_barrier();
+  } else {
+    {  // phase 0: no scores yet, only the copy of V_0
+      const Copy cp = next_copy();
 #pragma unroll
-      for (int i = 0; i < NL; ++i) copy_step(i, v0, g_off);
-      char* v_prev = vbuf0 + vslot(-1) * G::kTileBytes;
-      for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
-        *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the zeros are in LDS
+      for (int i = 0; i < NL; ++i) copy_step(i, cp, g_off);
     }
     phase_barrier();
-  }
-
-  // ---- 2 * (n_tiles + 1) phases, one barrier each.  The two groups run the
-  // same phases with their roles swapped; each has its own straight loop.
-  // Group 0 copies ring position t+2 during phase 2t+1 into the slot last read
-  // in phase 2t-1 and, before the barrier closing phase 2t+1, waits for
-  // position t+1 (its copy from phase 2t-1).  Group 1 copies position t during
-  // phase 2t (t >= 1) into the slot last read in phase 2t-1 and waits for it
-  // before the barrier closing phase 2t+1.  So K_{t+1} and V_t are in LDS
-  // before their first reader, phase 2t+2.  The copies past this item's tiles
-  // are the next item's first tiles.
-  if (grp == 0) {
-    for (int t = 0; t <= n_tiles; ++t) {
-      matrix_phase(t);  // phase 2t
-      phase_barrier();
-      softmax_phase(t, copy_for(t + 2));  // phase 2t + 1
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
-      phase_barrier();
-    }
-  } else {
-    for (int t = 0; t <= n_tiles; ++t) {
-      softmax_phase(t - 1, t == 0 ? Copy{nullptr, 0, nullptr} : copy_for(t));  // phase 2t
-      phase_barrier();
-      matrix_phase(t);  // phase 2t + 1
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
-      phase_barrier();
-    }
-  }
-
-  // ---- epilogue: O = acc / l (bf16, round to nearest even), lse = ln2 * (m + log2 l)
-  const int qi = q0w + col;
-  const float l_tot = sum_halves(l_run);
-  if (qi < S) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = O + head_off + (size_t)qi * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4_t v4 = {oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv,
-                            oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv};
-        *reinterpret_cast<bf16x4_t*>(orow + 32 * db + 8 * rg + 4 * half) = __builtin_convertvector(v4, bf16x4_t);
+    matrix_phase(0);  // phase 1
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+    phase_barrier();
+    for (;;) {
+      const Item nx = item_at(cur.k + 1);
+      for (int t = 0; t < cur.n_tiles; ++t, ++T) {
+        softmax_step(t, nx);  // phase 2T + 2
+        phase_barrier();
+        matrix_phase(T + 1);  // phase 2T + 3
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+        phase_barrier();
       }
-    if (LSE && half == 0) LSE[(size_t)bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
-  }
-  offK = (offK + n_tiles + 1) % G::kStagesK;
-  offV = (offV + n_tiles) % G::kStagesV;
-  if (!have_next) break;
-  bh = bh_n;
-  qb = qb_n;
+      prev = cur;
+      if (!nx.valid) break;
+      cur = nx;
+    }
+    finish_item(prev);
   }
   // no global->LDS copy may still be writing when the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
