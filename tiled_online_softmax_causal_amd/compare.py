@@ -1,7 +1,8 @@
 """Measured comparison of the tiled and the dense attention forward on one MI355X.
 
     python -m tiled_online_softmax_causal_amd.compare [--seq 1024,4096,16384,32768]
-        [--batch 1] [--heads 32] [--dim 128] [--paths flash,dense] [--steps 5] [--warmup 2]
+        [--batch 1] [--heads 32] [--dim 128] [--paths flash,dense] [--variants auto]
+        [--steps 5] [--warmup 2]
     python -m tiled_online_softmax_causal_amd.compare --traffic FETCH.csv WRITE.csv \\
         COPY_FETCH.csv COPY_WRITE.csv --calls N
 
@@ -11,7 +12,9 @@ length on seeded uniform(-0.8, 0.8) bf16 inputs, causal, and prints one JSON
 line per (S, path) with the measured time, TFLOP/s, effective GB/s of the
 compulsory bytes, and the logical bytes of the aiml.sh page's model
 (run-output.txt, hbm_traffic_sweep: b1 h32 d128, S = 1024 ... 32768) for the
-same shape.  The second form turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+same shape.  --variants times the tiled path once per kernel variant (the
+tilings of fa_fwd_variant: mfma_b256_k128, mfma_b256, mfma_b128, ...).  The
+second form turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 counter files of such a run into measured HBM bytes per call of each path,
 scaled by the counters of a plain device copy of known size
 (bench.py --copy-calibration).
@@ -84,6 +87,7 @@ def main():
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--dim", type=int, default=128)
     ap.add_argument("--paths", default="flash,dense")
+    ap.add_argument("--variants", default="auto", help="comma list of tiled-path variants (fa_fwd_variant)")
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--max-workspace-gib", type=float, default=64.0,
@@ -104,12 +108,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B, H, D = args.batch, args.heads, args.dim
-    paths = args.paths.split(",")
+    runs = []
+    for path in args.paths.split(","):
+        runs += [(path, v) for v in args.variants.split(",")] if path == "flash" else [(path, None)]
+    for v in args.variants.split(","):
+        if v not in fa.VARIANTS:
+            raise SystemExit(f"unknown variant {v}; one of {sorted(fa.VARIANTS)}")
     for S in (int(s) for s in args.seq.split(",")):
         q, k, v = uniform_qkv_device(B, H, S, D, seed=42, dtype=torch.bfloat16, device=dev)
         scale = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32).item())
         model = page_logical_traffic(S, num_heads=B * H, head_dim=D)
-        for path in paths:
+        for path, variant in runs:
             ws = None
             if path == "dense":
                 per_head = fa.dense_workspace_bytes(S)
@@ -119,7 +128,7 @@ def main():
             def call():
                 if path == "dense":
                     return fa.dense_fwd(q, k, v, causal=True, scale=scale, workspace=ws)
-                return fa.fwd(q, k, v, causal=True, scale=scale)
+                return fa.fwd(q, k, v, causal=True, scale=scale, variant=variant)
 
             for _ in range(args.warmup):
                 call()
@@ -134,7 +143,7 @@ def main():
             flops = attention_flops(B, H, S, D, True)
             nbytes = algorithmic_bytes(B, H, S, D, 2)
             print(json.dumps({
-                "path": path, "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
+                "path": path, "variant": variant, "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
                 "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
                 "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "compulsory_bytes": nbytes, "effective_gbs": round(nbytes / ms / 1e6, 1),
