@@ -20,6 +20,11 @@ Contents
             tiled_flash_attention takes its steps.  Pinned against ``dense``
             (agreement near 1e-16, as the page's equivalence check reports), the
             page's counters (tiles visited) and block-size invariance.
+``backward`` fp64 gradients (dQ, dK, dV) of that forward for an upstream dO,
+            the chain rule in plain numpy; not on the pages.  Pinned by
+            ``tests/test_oracle_backward.py`` against central finite
+            differences of ``dense``, invariants and closed forms.
 """
 from .dense import attention_dense, build_library, library_path  # noqa: F401
 from .tiled import tiled_attention  # noqa: F401
+from .backward import attention_backward, row_deltas  # noqa: F401
