@@ -141,6 +141,48 @@ fa_status fa_dense_fwd(const void *q, const void *k, const void *v, void *o, flo
  * a multiple of 8 elements; 0 for S < 1.  Host-only. */
 int64_t fa_dense_workspace_bytes(int64_t S);
 
+/*
+ * fa_bwd -- gradients of the fa_fwd forward: dQ, dK, dV for an upstream
+ * gradient dO of O.  The pages stop at the forward of the aiml.sh page "Speed
+ * up long contexts with FlashAttention" (lab.py, tiled_flash_attention); this
+ * is that forward differentiated, computed the same tiled way.  Per (batch,
+ * head), with P = softmax(scale * Q K^T) under the causal rule:
+ *
+ *     delta_i = dO_i . O_i,  dP = dO V^T,  dS = P * (dP - delta)
+ *     dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO
+ *
+ * P is recomputed tile by tile from Q, K and lse, so no S x S matrix reaches
+ * memory.  Two kernels run on `stream`: one per block of 128 query rows (dQ,
+ * and delta into the workspace), then one per block of 128 keys (dK, dV).
+ *
+ *   q, k, v    in : [B, H, S, D] bf16, the forward's inputs
+ *   o, lse     in : the forward's outputs for the same causal and scale (o
+ *                   [B, H, S, D] bf16, lse [B, H, S] fp32, natural log)
+ *   dout       in : [B, H, S, D] bf16, the gradient of o
+ *   dq, dk, dv out: [B, H, S, D] bf16; must not overlap any input (not checked)
+ *   B, H, S, causal, scale, stream: as for fa_fwd
+ *   D          64 or 128
+ *   dtype      FA_DTYPE_BF16 only.  P and dS are rounded to bf16 as MFMA
+ *              operands; sums are fp32
+ *   workspace  device memory owned by the caller, 4-byte aligned, at least
+ *              fa_bwd_workspace_bytes(B, H, S) bytes; its contents on return
+ *              are the row dot products delta (fp32 [B, H, S]).  Calls that
+ *              share a workspace must be ordered on one stream.
+ *
+ * All pointers are device pointers, 16-byte aligned (lse and workspace: 4).
+ * Returns FA_OK, FA_ERR_INVALID_ARGUMENT (NULL or misaligned pointer, B, H, S
+ * or D < 1, non-finite scale, workspace too small), FA_ERR_UNSUPPORTED (dtype,
+ * D, or S * D >= 2^31) or FA_ERR_HIP.
+ */
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t S,
+                 int64_t D, int causal, float scale, fa_dtype dtype, void *workspace,
+                 int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_bwd needs: B * H * S fp32 values; 0 if B, H or S < 1.
+ * Host-only. */
+int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S);
+
 /* Static, never-NULL description of a status code. */
 const char *fa_status_str(fa_status status);
 

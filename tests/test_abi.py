@@ -141,3 +141,35 @@ def test_dense_rejects_before_launch():
     assert _dense(dtype=fa.FA_DTYPE_FP32) == fa.FA_ERR_UNSUPPORTED         # bf16 only
     assert _dense(D=32) == fa.FA_ERR_UNSUPPORTED                           # D 64 or 128
     assert _dense(dtype=7) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_bytes():
+    """One fp32 row dot product per (batch, head, row)."""
+    assert fa.bwd_workspace_bytes(0, 1, 5) == 0
+    assert fa.bwd_workspace_bytes(2, 3, 0) == 0
+    assert fa.bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 4
+    assert fa.bwd_workspace_bytes(8, 32, 8192) == 8 * 32 * 8192 * 4
+
+
+def _bwd(ws=P, ws_bytes=1 << 40, dtype=fa.FA_DTYPE_BF16, D=128, ptrs=(P,) * 9, B=1, H=1, S=64, scale=0.1):
+    return fa.fa_bwd_raw(*ptrs, B, H, S, D, True, scale, dtype, ws, ws_bytes)
+
+
+def test_bwd_rejects_before_launch():
+    """Every invalid call returns its status on the host; nothing is launched (no GPU here)."""
+    assert _bwd(ws=0) == fa.FA_ERR_INVALID_ARGUMENT                                 # no workspace
+    assert _bwd(ws_bytes=fa.bwd_workspace_bytes(1, 1, 64) - 4) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _bwd(ws=P + 2) == fa.FA_ERR_INVALID_ARGUMENT                             # misaligned workspace
+    for i in range(9):                                                               # each pointer NULL
+        ptrs = [P] * 9
+        ptrs[i] = 0
+        assert _bwd(ptrs=tuple(ptrs)) == fa.FA_ERR_INVALID_ARGUMENT, i
+    ptrs = [P] * 9
+    ptrs[6] = P + 8                                                                  # misaligned dq
+    assert _bwd(ptrs=tuple(ptrs)) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _bwd(B=0) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _bwd(S=0) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _bwd(scale=float("inf")) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _bwd(dtype=fa.FA_DTYPE_FP32) == fa.FA_ERR_UNSUPPORTED                    # bf16 only
+    assert _bwd(D=32) == fa.FA_ERR_UNSUPPORTED                                      # D 64 or 128
+    assert _bwd(S=1 << 24, D=128) == fa.FA_ERR_UNSUPPORTED                          # S * D >= 2^31

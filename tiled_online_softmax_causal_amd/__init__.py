@@ -23,8 +23,8 @@ VARIANTS = {"auto": 0, "mfma_b256": 1, "mfma_b128": 2, "valu": 3, "mfma_b256_k12
 
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_fwd_select_variant", "fa_fwd_tiles_per_head",
-           "fa_dense_fwd", "fa_dense_workspace_bytes", "fa_status_str", "fa_last_hip_error",
-           "fa_version")
+           "fa_dense_fwd", "fa_dense_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
+           "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
 
@@ -56,6 +56,10 @@ def load_library(path: str = LIBRARY_PATH):
     lib.fa_dense_fwd.restype = i32
     lib.fa_dense_workspace_bytes.argtypes = [i64]
     lib.fa_dense_workspace_bytes.restype = i64
+    lib.fa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, p, i64, p]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.fa_bwd_workspace_bytes.restype = i64
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -216,3 +220,57 @@ def dense_fwd(q, k, v, causal: bool = True, scale: float | None = None, workspac
                                   workspace.data_ptr(), workspace.numel(), st)
     _check(status)
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, S: int) -> int:
+    """Workspace bytes fa_bwd needs: one fp32 row dot product dO_i . O_i per (batch, head, row)."""
+    return load_library().fa_bwd_workspace_bytes(B, H, S)
+
+
+def fa_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, do_ptr: int, dq_ptr: int,
+               dk_ptr: int, dv_ptr: int, B: int, H: int, S: int, D: int, causal: bool, scale: float,
+               dtype: int, ws_ptr: int, ws_bytes: int, stream: int = 0) -> int:
+    """Call fa_bwd with raw device addresses; returns the fa_status code."""
+    lib = load_library()
+    return lib.fa_bwd(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None, lse_ptr or None,
+                      do_ptr or None, dq_ptr or None, dk_ptr or None, dv_ptr or None, B, H, S, D,
+                      int(bool(causal)), float(scale), dtype, ws_ptr or None, int(ws_bytes), stream or None)
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, workspace=None, stream=None):
+    """Gradients ``(dq, dk, dv)`` of the forward on ``[B, H, S, D]`` bf16 CUDA tensors.
+
+    ``o`` and ``lse`` are the forward's outputs (:func:`fwd` with the same
+    ``causal`` and ``scale``), ``do`` the upstream gradient of ``o``.
+    ``workspace`` is an fp32 (or uint8) CUDA tensor of at least
+    :func:`bwd_workspace_bytes` bytes; without one it is allocated here, the
+    library itself allocates nothing.
+    """
+    import torch
+
+    ts = (("q", q), ("k", k), ("v", v), ("o", o), ("do", do))
+    if q.dim() != 4 or any(t.shape != q.shape for _, t in ts):
+        raise ValueError("q, k, v, o, do must share one [B, H, S, D] shape")
+    if any(not t.is_cuda or t.dtype != torch.bfloat16 for _, t in ts):
+        raise ValueError("q, k, v, o, do must be bf16 device tensors")
+    for name, t in ts:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, S, D = q.shape
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous fp32 [B, H, S] device tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = torch.empty(B * H * S, dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        status = fa_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, S, D, causal,
+                            scale, FA_DTYPE_BF16, workspace.data_ptr(), ws_bytes, st)
+    _check(status)
+    return dq, dk, dv

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "fa_bwd.h"
 #include "fa_dense.h"
 #include "fa_fwd_pingpong.h"
 #include "fa_mfma_bf16.h"
@@ -163,6 +164,27 @@ hipError_t launch_dense(const void* q, const void* k, const void* v, void* o, fl
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int64_t BH, int64_t S, float scale,
+                      float* delta, hipStream_t stream) {
+  namespace bw = fa::bwd;
+  const int64_t nb = ceil_div(S, bw::kRows);  // query blocks (dQ) and key blocks (dK/dV) per head
+  const int64_t grid = BH * nb;
+  const int xcd_group = (BH % kNumXcd) == 0;
+  const auto* Q = static_cast<const uint16_t*>(q);
+  const auto* K = static_cast<const uint16_t*>(k);
+  const auto* V = static_cast<const uint16_t*>(v);
+  const auto* dO = static_cast<const uint16_t*>(dout);
+  hipLaunchKernelGGL((bw::attn_bwd_dq<D, CAUSAL>), dim3((unsigned)grid), dim3(fa::kThreads), 0, stream, Q, K, V,
+                     static_cast<const uint16_t*>(o), dO, lse, static_cast<uint16_t*>(dq), delta, (int)S, (int)nb,
+                     (int)BH, scale, xcd_group);
+  hipLaunchKernelGGL((bw::attn_bwd_dkdv<D, CAUSAL>), dim3((unsigned)grid), dim3(fa::kThreads), 0, stream, Q, K, V,
+                     dO, lse, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), (int)S, (int)nb,
+                     (int)BH, scale, xcd_group);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,6 +309,40 @@ fa_status fa_dense_fwd(const void* q, const void* k, const void* v, void* o, flo
       g_last_hip_error = static_cast<int>(err);
       return FA_ERR_HIP;
     }
+  }
+  return FA_OK;
+}
+
+int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S) {
+  return (B < 1 || H < 1 || S < 1) ? 0 : B * H * S * (int64_t)sizeof(float);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale,
+                 fa_dtype dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARGUMENT;
+  if (B < 1 || H < 1 || S < 1 || D < 1) return FA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(workspace, 4))
+    return FA_ERR_INVALID_ARGUMENT;
+  if (dtype != FA_DTYPE_BF16 || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  if (S * D >= (int64_t(1) << 31) || B > INT32_MAX / H) return FA_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  if (BH * ceil_div(S, fa::bwd::kRows) > INT32_MAX || BH * S >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, S)) return FA_ERR_INVALID_ARGUMENT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* delta = static_cast<float*>(workspace);
+  hipError_t err;
+  if (D == 128)
+    err = causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, S, scale, delta, st)
+                 : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, S, scale, delta, st);
+  else
+    err = causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, BH, S, scale, delta, st)
+                 : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, BH, S, scale, delta, st);
+  if (err != hipSuccess) {
+    g_last_hip_error = static_cast<int>(err);
+    return FA_ERR_HIP;
   }
   return FA_OK;
 }

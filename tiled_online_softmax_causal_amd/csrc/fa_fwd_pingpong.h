@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
                               oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv};
           *reinterpret_cast<bf16x4_t*>(orow + 32 * db + 8 * rg + 4 * half) = __builtin_convertvector(v4, bf16x4_t);
         }
-      if (LSE && half == 0) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+      if (LSE && half == 0) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * common::kLn2;
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
