@@ -14,7 +14,10 @@ compulsory bytes, and the logical bytes of the aiml.sh page's model
 (run-output.txt, hbm_traffic_sweep: b1 h32 d128, S = 1024 ... 32768) for the
 same shape.  --variants times the tiled path once per kernel variant (the
 tilings of fa_fwd_variant: mfma_b256_k128, mfma_b256, mfma_b128, ...).  The
-second form turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+path "bwd" times fa_bwd (the forward's O and LSE and a seeded dO resident);
+its TFLOP/s count the five products of the gradient, 2.5x the forward's flops,
+and "executed_tflops" the seven its two kernels run (each recomputes P and
+dP).  The second form turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 counter files of such a run into measured HBM bytes per call of each path,
 scaled by the counters of a plain device copy of known size
 (bench.py --copy-calibration).
@@ -40,6 +43,8 @@ def _path_of(kernel_name: str):
         return "flash"
     if "dense_" in kernel_name:
         return "dense"
+    if "attn_bwd" in kernel_name:
+        return "bwd"
     return None
 
 
@@ -120,12 +125,19 @@ def main():
         model = page_logical_traffic(S, num_heads=B * H, head_dim=D)
         for path, variant in runs:
             ws = None
+            if path == "bwd":
+                o, lse = fa.fwd(q, k, v, causal=True, scale=scale)
+                do, _, _ = uniform_qkv_device(B, H, S, D, seed=1042, low=-1.0, high=1.0, dtype=torch.bfloat16,
+                                              device=dev)
+                ws = torch.empty(B * H * S, dtype=torch.float32, device=dev)
             if path == "dense":
                 per_head = fa.dense_workspace_bytes(S)
                 n = max(1, min(B * H, int(args.max_workspace_gib * 2**30) // per_head))
                 ws = torch.empty(n * per_head, dtype=torch.uint8, device=dev)
 
             def call():
+                if path == "bwd":
+                    return fa.bwd(q, k, v, o, lse, do, causal=True, scale=scale, workspace=ws)
                 if path == "dense":
                     return fa.dense_fwd(q, k, v, causal=True, scale=scale, workspace=ws)
                 return fa.fwd(q, k, v, causal=True, scale=scale, variant=variant)
@@ -140,14 +152,16 @@ def main():
             ev1.record()
             torch.cuda.synchronize()
             ms = ev0.elapsed_time(ev1) / args.steps
-            flops = attention_flops(B, H, S, D, True)
-            nbytes = algorithmic_bytes(B, H, S, D, 2)
+            flops = attention_flops(B, H, S, D, True) * (2.5 if path == "bwd" else 1.0)
+            # bwd reads Q, K, V, O, dO and writes dQ, dK, dV (plus LSE and delta)
+            nbytes = algorithmic_bytes(B, H, S, D, 2) * (2 if path == "bwd" else 1)
             print(json.dumps({
                 "path": path, "variant": variant, "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
                 "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
                 "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "compulsory_bytes": nbytes, "effective_gbs": round(nbytes / ms / 1e6, 1),
-                "dense_workspace_heads": None if ws is None else ws.numel() // fa.dense_workspace_bytes(S),
+                "executed_tflops": round(flops * 1.4 / ms / 1e9, 1) if path == "bwd" else None,
+                "dense_workspace_heads": None if (ws is None or path != "dense") else ws.numel() // fa.dense_workspace_bytes(S),
                 "page_model_mb": {"standard_total": round(model["standard_total_bytes"] / 1e6, 2),
                                   "tiled_logical": round(model["tiled_logical_bytes"] / 1e6, 2),
                                   "qkvo_compulsory": round(model["qkvo_bytes"] / 1e6, 2)},
