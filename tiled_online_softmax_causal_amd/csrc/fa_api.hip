@@ -176,10 +176,15 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   const auto* K = static_cast<const uint16_t*>(k);
   const auto* V = static_cast<const uint16_t*>(v);
   const auto* dO = static_cast<const uint16_t*>(dout);
-  hipLaunchKernelGGL((bw::attn_bwd_dq<D, CAUSAL>), dim3((unsigned)grid), dim3(fa::kThreads), 0, stream, Q, K, V,
+  // two workgroups per CU (two waves per SIMD), so one wave's exponentials and
+  // dS products overlap the other's MFMAs.  At d = 128 the key-side kernel fits
+  // that register budget only with 32-row query tiles (it still spills 16
+  // VGPRs of its K operand, reloaded once per tile).
+  constexpr int kOcc = 2, kQT = D == 128 ? 32 : 64;
+  hipLaunchKernelGGL((bw::attn_bwd_dq<D, CAUSAL, kOcc>), dim3((unsigned)grid), dim3(fa::kThreads), 0, stream, Q, K, V,
                      static_cast<const uint16_t*>(o), dO, lse, static_cast<uint16_t*>(dq), delta, (int)S, (int)nb,
                      (int)BH, scale, xcd_group);
-  hipLaunchKernelGGL((bw::attn_bwd_dkdv<D, CAUSAL>), dim3((unsigned)grid), dim3(fa::kThreads), 0, stream, Q, K, V,
+  hipLaunchKernelGGL((bw::attn_bwd_dkdv<D, CAUSAL, kQT, kOcc>), dim3((unsigned)grid), dim3(fa::kThreads), 0, stream, Q, K, V,
                      dO, lse, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), (int)S, (int)nb,
                      (int)BH, scale, xcd_group);
   return hipGetLastError();

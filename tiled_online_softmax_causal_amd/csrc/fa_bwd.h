@@ -33,6 +33,7 @@
 // in the matching row order.
 #pragma once
 
+#include "fa_common.h"
 #include "fa_mfma_bf16.h"
 
 namespace fa {
@@ -42,6 +43,27 @@ constexpr int kRows = 32 * kWaves;  // query rows (dQ kernel) or keys (dK/dV ker
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// Copy ROWS rows of X starting at r0 (rows past S re-read row S-1) into a
+// swizzled LDS tile, HBM -> LDS directly (global_load_lds, no register
+// staging): thread tid fills the tile's 16-byte slots tid, tid + 256, ...
+// with the logical chunk the swizzle puts there.  The copies are not tracked
+// by the compiler; the caller waits (s_waitcnt vmcnt(0)) before the barrier
+// that publishes the tile.
+template <int D, int ROWS>
+__device__ __forceinline__ void copy_tile(const uint16_t* __restrict__ X, int r0, int S, char* tile, int tid) {
+  constexpr int kChunks = D / 8;
+  constexpr int L = ROWS * kChunks / kThreads;
+  static_assert(ROWS * kChunks % kThreads == 0, "a tile must split evenly over the workgroup");
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int cidx = i * kThreads + tid;
+    const int row = cidx / kChunks, pch = cidx % kChunks;
+    const int lch = pch ^ lds_swizzle<D>(row);
+    common::copy16_to_lds(X + (size_t)min(r0 + row, S - 1) * D + lch * 8, tile + (i * kThreads + wave * 64) * 16);
+  }
+}
 
 // A 32-row operand in registers: lane holds X[row][16*ds + 8*half + 0..7].
 template <int D>
@@ -98,8 +120,8 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ Y, size_t row_o
 }
 
 // ---------------------------------------------------------------- dQ (and delta)
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
+template <int D, bool CAUSAL, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     uint16_t* __restrict__ dQ, float* __restrict__ Delta, int S, int n_qb, int BH, float scale, int xcd_group) {
@@ -136,15 +158,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
 
   const int kv_end = CAUSAL ? min(S, q0 + kRows) : S;
   const int n_tiles = (kv_end + kBK - 1) / kBK;
-  TileStager<D> stager;
-  stager.load(K + head, V + head, 0, S, tid);
-  stager.store(lds, tid);
+  copy_tile<D, kBK>(K + head, 0, S, lds, tid);
+  copy_tile<D, kBK>(V + head, 0, S, lds + G::kTileBytes, tid);
+  __builtin_amdgcn_s_waitcnt(common::waitcnt_vm<0>());
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int kv0 = t * kBK;
     const bool has_next = t + 1 < n_tiles;
-    if (has_next) stager.load(K + head, V + head, kv0 + kBK, S, tid);
+    if (has_next) {  // into the other stage, last read before the previous barrier
+      char* nx = lds + ((t + 1) & 1) * G::kStageBytes;
+      copy_tile<D, kBK>(K + head, kv0 + kBK, S, nx, tid);
+      copy_tile<D, kBK>(V + head, kv0 + kBK, S, nx + G::kTileBytes, tid);
+    }
     const char* Kl = lds + (t & 1) * G::kStageBytes;
     const char* Vl = Kl + G::kTileBytes;
 
@@ -181,22 +207,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq(
           qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_transposed<D>(Kl, db, ks, lane), dsb, qacc[db], 0, 0, 0);
       }
     }
-    if (has_next) stager.store(lds + ((t + 1) & 1) * G::kStageBytes, tid);
+    __builtin_amdgcn_s_waitcnt(common::waitcnt_vm<0>());  // the next tile has landed
     __syncthreads();
   }
   if (qi < S) store_row<D>(dQ, head + (size_t)qi * D, qacc, scale, half);
 }
 
 // ---------------------------------------------------------------- dK and dV
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
+// QT query rows per streamed tile (32 or 64): the shorter tile needs half the
+// accumulator registers for X and dP, at twice the barriers.
+template <int D, int QT>
+struct QTileGeo {
+  static constexpr int kTileBytes = QT * D * 2;
+  static constexpr int kStageBytes = 2 * kTileBytes;  // Q tile then dO tile
+  static constexpr int kLdsBytes = 2 * kStageBytes;   // two stages
+};
+
+template <int D, bool CAUSAL, int QT, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int S, int n_kb, int BH, float scale, int xcd_group) {
-  using G = TileGeo<D>;
-  constexpr int DS = D / 16, DB = D / 32, QB = kBK / 32, KS = kBK / 16;
+  using G = QTileGeo<D, QT>;
+  constexpr int DS = D / 16, DB = D / 32, QB = QT / 32, KS = QT / 16;
+  static_assert(QT == 32 || QT == 64, "query tiles of 32 or 64 rows");
   __shared__ __attribute__((aligned(16))) char lds[G::kLdsBytes];
-  __shared__ __attribute__((aligned(16))) float rows[2][2][kBK];  // per stage: lse * log2(e), delta
+  __shared__ __attribute__((aligned(16))) float rows[2][2][QT];  // per stage: lse * log2(e), delta
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -222,30 +258,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
     dvacc[db] = (f32x16_t){};
   }
 
-  const int n_qt = (S + kBK - 1) / kBK;
-  const int t0 = CAUSAL ? j0 / kBK : 0;  // the first query tile that sees a key of this block
-  auto row_value = [&](int q0n) {        // threads 0-63: lse * log2(e), 64-127: delta of row q0n + tid % 64
-    const size_t r = hrow + min(q0n + (tid & 63), S - 1);
-    return tid < 64 ? LSE[r] * kLog2e : (tid < 128 ? Delta[r] : 0.f);
+  const int n_qt = (S + QT - 1) / QT;
+  const int t0 = CAUSAL ? j0 / QT : 0;  // the first query tile that sees a key of this block
+  // per-row values of a tile: threads 0..QT-1 lse * log2(e), QT..2QT-1 delta
+  auto row_value = [&](int q0n) {
+    const size_t r = hrow + min(q0n + tid % QT, S - 1);
+    return tid < QT ? LSE[r] * kLog2e : (tid < 2 * QT ? Delta[r] : 0.f);
   };
-  TileStager<D> stager;
-  stager.load(Q + head, dO + head, t0 * kBK, S, tid);
-  float rv = row_value(t0 * kBK);
-  stager.store(lds, tid);
-  if (tid < 128) rows[0][tid >> 6][tid & 63] = rv;
+  auto copy_stage = [&](int q0n, int stage) {
+    char* st = lds + stage * G::kStageBytes;
+    copy_tile<D, QT>(Q + head, q0n, S, st, tid);
+    copy_tile<D, QT>(dO + head, q0n, S, st + G::kTileBytes, tid);
+  };
+  copy_stage(t0 * QT, 0);
+  float rv = row_value(t0 * QT);
+  if (tid < 2 * QT) rows[0][tid / QT][tid % QT] = rv;
+  __builtin_amdgcn_s_waitcnt(common::waitcnt_vm<0>());
   __syncthreads();
 
   for (int t = t0; t < n_qt; ++t) {
-    const int q0 = t * kBK, st = (t - t0) & 1;
+    const int q0 = t * QT, st = (t - t0) & 1;
     const bool has_next = t + 1 < n_qt;
-    if (has_next) {
-      stager.load(Q + head, dO + head, q0 + kBK, S, tid);
-      rv = row_value(q0 + kBK);
+    if (has_next) {  // into the other stage, last read before the previous barrier
+      copy_stage(q0 + QT, st ^ 1);
+      rv = row_value(q0 + QT);
     }
     const char* Ql = lds + st * G::kStageBytes;
     const char* dOl = Ql + G::kTileBytes;
 
-    const bool live = (!CAUSAL || q0 + kBK - 1 >= j0w) && j0w < S;
+    const bool live = (!CAUSAL || q0 + QT - 1 >= j0w) && j0w < S;
     if (live) {
       // X = Q K^T and dP = dO V^T (queries down the registers, one key per lane)
       f32x16_t xacc[QB], pacc[QB];
@@ -289,10 +330,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv(
         }
       }
     }
-    if (has_next) {
-      stager.store(lds + (st ^ 1) * G::kStageBytes, tid);
-      if (tid < 128) rows[st ^ 1][tid >> 6][tid & 63] = rv;
-    }
+    if (has_next && tid < 2 * QT) rows[st ^ 1][tid / QT][tid % QT] = rv;
+    __builtin_amdgcn_s_waitcnt(common::waitcnt_vm<0>());  // the next tiles have landed
     __syncthreads();
   }
   if (kj < S) {
