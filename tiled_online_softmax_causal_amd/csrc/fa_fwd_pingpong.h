@@ -323,23 +323,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   // adds exactly 0; the scores of phase N (past the last tile) are never used.
 
   // ---- epilogue of an item: O = acc / l (bf16, round to nearest even),
-  // lse = ln2 * (m + log2 l); then the state starts over for the next item
+  // lse = ln2 * (m + log2 l); then the state starts over for the next item.
+  // In the accumulator layout lanes l and l^32 hold the two 8-byte halves of
+  // each 16-byte piece of one row; one v_permlane32_swap per dword hands each
+  // lane a whole piece of its own and its partner's, so every store writes 32
+  // contiguous bytes of each of 32 rows (8 stores instead of 16 of 16 bytes).
   auto finish_item = [&](const Item& it) {
     const int qi = it.qb * kBQ + wave * kQW + col;
     const float l_tot = sum_halves(l_run);
-    if (qi < S) {
-      const float inv = 1.0f / l_tot;
-      uint16_t* orow = O + (size_t)it.bh * S * D + (size_t)qi * D;
+    const float inv = 1.0f / l_tot;  // rows past S (l = 0) are not stored
+    uint16_t* const orow = O + (size_t)it.bh * S * D + (size_t)min(qi, S - 1) * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const f32x4_t v4 = {oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv,
-                              oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv};
-          *reinterpret_cast<bf16x4_t*>(orow + 32 * db + 8 * rg + 4 * half) = __builtin_convertvector(v4, bf16x4_t);
+      for (int rg = 0; rg < 4; rg += 2) {
+        const f32x4_t v0 = {oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv,
+                            oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv};
+        const f32x4_t v1 = {oacc[db][4 * rg + 4] * inv, oacc[db][4 * rg + 5] * inv,
+                            oacc[db][4 * rg + 6] * inv, oacc[db][4 * rg + 7] * inv};
+        // a0: columns 32db + 8rg + 4half + 0..3, a1: the same for rg + 1
+        const u32x2_t a0 = __builtin_bit_cast(u32x2_t, __builtin_convertvector(v0, bf16x4_t));
+        const u32x2_t a1 = __builtin_bit_cast(u32x2_t, __builtin_convertvector(v1, bf16x4_t));
+        // the lower half-wave keeps piece rg and needs its partner's a0; the
+        // upper keeps piece rg + 1 and needs its partner's a1
+        u32x2_t got;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const unsigned send = half ? a0[e] : a1[e];
+          const auto p = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+          got[e] = half ? p[0] : p[1];
         }
-      if (LSE && half == 0) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * common::kLn2;
-    }
+        const u32x4_t piece = half ? (u32x4_t){got[0], got[1], a1[0], a1[1]} : (u32x4_t){a0[0], a0[1], got[0], got[1]};
+        if (qi < S) *reinterpret_cast<u32x4_t*>(orow + 32 * db + 8 * (rg + half)) = piece;
+      }
+    if (LSE && half == 0 && qi < S) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * common::kLn2;
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
     m_run = -__builtin_inff();
