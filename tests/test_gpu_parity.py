@@ -217,6 +217,15 @@ def test_b1_h32_s32768_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("B,H,S,n_rows", [(1, 2, 131072, 48), (1, 1, 1 << 20, 24)])
+def test_long_sequences_sampled(B, H, S, n_rows):
+    """The end of the measured sweep (S = 131072) and S = 2^20, where row offsets
+    reach 2^27 elements; sampled rows always include the last ones."""
+    case(f"bf16 {B}x{H}x{S}x128 causal, {n_rows} rows per head")
+    _sampled_check(B, H, S, 128, True, list(range(B * H)), n_rows)
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("B,H,S", [(1, 5, 16384), (2, 8, 5000)])
 def test_resident_grid_sequences(B, H, S):
     """More work items than CUs, so one resident workgroup per CU walks a sequence of
