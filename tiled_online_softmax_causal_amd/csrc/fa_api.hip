@@ -178,8 +178,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   const auto* dO = static_cast<const uint16_t*>(dout);
   // two workgroups per CU (two waves per SIMD), so one wave's exponentials and
   // dS products overlap the other's MFMAs.  At d = 128 the key-side kernel fits
-  // that register budget only with 32-row query tiles (it still spills 16
-  // VGPRs of its K operand, reloaded once per tile).
+  // that register budget only with 32-row query tiles.
   constexpr int kOcc = 2, kQT = D == 128 ? 32 : 64;
   hipLaunchKernelGGL((bw::attn_bwd_dq<D, CAUSAL, kOcc>), dim3((unsigned)grid), dim3(fa::kThreads), 0, stream, Q, K, V,
                      static_cast<const uint16_t*>(o), dO, lse, static_cast<uint16_t*>(dq), delta, (int)S, (int)nb,

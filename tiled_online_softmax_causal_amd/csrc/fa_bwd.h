@@ -17,9 +17,10 @@
 //   attn_bwd_dq    a workgroup owns 128 query rows (32 per wave) and streams
 //                  64-key K/V tiles: S^T = K Q^T and dP^T = V dO^T, then
 //                  dQ^T += K^T dS^T.  It also writes delta for the second kernel.
-//   attn_bwd_dkdv  a workgroup owns 128 keys (32 per wave) and streams 64-row
-//                  Q/dO tiles: X = Q K^T and dP = dO V^T, then dV^T += dO^T P
-//                  and dK^T += Q^T dS.
+//   attn_bwd_dkdv  a workgroup owns 128 keys (32 per wave; their K rows in LDS,
+//                  their V rows in registers) and streams 32- or 64-row Q/dO
+//                  tiles: X = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//                  dK^T += Q^T dS.
 // Both recompute P and dP, which costs two extra products per tile over a
 // one-kernel design with atomic dQ updates.
 //
@@ -233,6 +234,9 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dkdv(
   static_assert(QT == 32 || QT == 64, "query tiles of 32 or 64 rows");
   __shared__ __attribute__((aligned(16))) char lds[G::kLdsBytes];
   __shared__ __attribute__((aligned(16))) float rows[2][2][QT];  // per stage: lse * log2(e), delta
+  // the workgroup's 128 K rows (swizzled like the tiles): the B operand of
+  // X = Q K^T, read from LDS each tile instead of held in registers
+  __shared__ __attribute__((aligned(16))) char kl[kRows * D * 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -246,9 +250,9 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dkdv(
   const int kj = j0w + col, kr = min(kj, S - 1);
 
   // K^T and V^T operands of the lane's key (the B side of X = Q K^T, dP = dO V^T)
-  bf16x8_t kreg[DS], vreg[DS];
-  load_row_operand<D>(kreg, K, head + (size_t)kr * D, half);
+  bf16x8_t vreg[DS];
   load_row_operand<D>(vreg, V, head + (size_t)kr * D, half);
+  copy_tile<D, kRows>(K + head, j0, S, kl, tid);
   const float c2 = scale * kLog2e;
 
   f32x16_t dkacc[DB], dvacc[DB];
@@ -296,7 +300,8 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dkdv(
         pacc[qb] = (f32x16_t){};
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          xacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_rows<D>(Ql, qb, ds, col, half), kreg[ds], xacc[qb], 0, 0, 0);
+          xacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_rows<D>(Ql, qb, ds, col, half),
+                                                              tile_rows<D>(kl, wave, ds, col, half), xacc[qb], 0, 0, 0);
           pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_rows<D>(dOl, qb, ds, col, half), vreg[ds], pacc[qb], 0, 0, 0);
         }
       }
