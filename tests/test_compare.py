@@ -1,4 +1,4 @@
-"""Host logic of the tiled-vs-dense comparison: rocprofv3 counter files -> HBM bytes per call.
+"""Host logic of the tiled-vs-dense comparison: rocprofv3 counter files -> HBM bytes per call and GPU clock.
 
 Synthetic counter files: a 1 GiB device copy whose FETCH_SIZE reads 0.5 GiB and
 whose WRITE_SIZE reads 1 GiB (so the scale factors are 2 and 1, as measured on
@@ -6,7 +6,7 @@ gfx950), and one call of each path with known counter values.
 """
 import csv
 
-from tiled_online_softmax_causal_amd.compare import traffic
+from tiled_online_softmax_causal_amd.compare import clock, traffic
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 
@@ -45,3 +45,20 @@ def test_counters_scaled_by_copy_calibration(tmp_path):
     halved = traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
                      str(tmp_path / "cw.csv"), calls=2)
     assert halved["dense"]["total_bytes"] == out["dense"]["total_bytes"] // 2
+
+
+def test_clock_from_busy_cycles(tmp_path):
+    """GRBM_GUI_ACTIVE is summed over the 8 XCDs: 8 * 1.6e6 busy cycles in 1 ms is 1.6 GHz."""
+    fields = FIELDS + ["Start_Timestamp", "End_Timestamp"]
+    with open(tmp_path / "g.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        rows = [("void fa::pp::attn_fwd_pingpong<128, 128, true>(...)", 8 * 1.6e6, 1_000_000),
+                ("void fa::pp::attn_fwd_pingpong<128, 128, true>(...)", 8 * 2.0e6, 1_000_000),
+                ("void fa::bwd::attn_bwd_dq<128, true, 2>(...)", 8 * 1.0e6, 500_000),
+                ("distribution_elementwise_grid_stride_kernel", 1.0, 10)]
+        for i, (name, value, ns) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": "GRBM_GUI_ACTIVE",
+                        "Counter_Value": value, "Start_Timestamp": 1000, "End_Timestamp": 1000 + ns})
+    out = clock(str(tmp_path / "g.csv"))
+    assert out == {"bwd": {"ghz": 2.0, "dispatches": 1}, "flash": {"ghz": 1.8, "dispatches": 2}}

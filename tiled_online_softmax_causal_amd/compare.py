@@ -85,6 +85,24 @@ def traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv:
     return out
 
 
+def clock(grbm_csv: str, n_xcd: int = 8) -> dict:
+    """Mean GPU clock (GHz) over each path's dispatches: GRBM_GUI_ACTIVE, the cycles the
+    graphics engine is busy, summed over the n_xcd XCDs, divided by the dispatch's duration."""
+    acc = {}
+    with open(grbm_csv) as f:
+        for r in csv.DictReader(f):
+            key = _path_of(r["Kernel_Name"])
+            if key is None or r["Counter_Name"] != "GRBM_GUI_ACTIVE":
+                continue
+            ns = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            if ns <= 0:
+                continue
+            ghz = float(r["Counter_Value"]) / n_xcd / ns
+            s, n = acc.get(key, (0.0, 0))
+            acc[key] = (s + ghz, n + 1)
+    return {k: {"ghz": round(s / n, 3), "dispatches": n} for k, (s, n) in sorted(acc.items())}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--seq", default="1024,4096,16384,32768")
@@ -99,7 +117,15 @@ def main():
                     help="workspace of the dense path; heads are processed in chunks that fit")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     ap.add_argument("--calls", type=int, default=1, help="attention calls per path in the profiled run")
+    ap.add_argument("--inputs", choices=("uniform", "zeros"), default="uniform",
+                    help="uniform(-0.8, 0.8) (the workload) or all-zero Q, K, V: the same instructions with "
+                         "no switching in the matrix-core operands, to separate power from issue limits")
+    ap.add_argument("--clock", metavar="GRBM_CSV",
+                    help="rocprofv3 --pmc GRBM_GUI_ACTIVE counter file -> mean GPU clock of each path's kernels")
     args = ap.parse_args()
+    if args.clock:
+        print(json.dumps(clock(args.clock)))
+        return
     if args.traffic:
         print(json.dumps(traffic(*args.traffic, calls=args.calls)))
         return
@@ -121,6 +147,9 @@ def main():
             raise SystemExit(f"unknown variant {v}; one of {sorted(fa.VARIANTS)}")
     for S in (int(s) for s in args.seq.split(",")):
         q, k, v = uniform_qkv_device(B, H, S, D, seed=42, dtype=torch.bfloat16, device=dev)
+        if args.inputs == "zeros":
+            for t in (q, k, v):
+                t.zero_()
         scale = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32).item())
         model = page_logical_traffic(S, num_heads=B * H, head_dim=D)
         for path, variant in runs:
@@ -156,7 +185,7 @@ def main():
             # bwd reads Q, K, V, O, dO and writes dQ, dK, dV (plus LSE and delta)
             nbytes = algorithmic_bytes(B, H, S, D, 2) * (2 if path == "bwd" else 1)
             print(json.dumps({
-                "path": path, "variant": variant, "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
+                "path": path, "variant": variant, "inputs": args.inputs, "batch": B, "heads": H, "seq_len": S, "head_dim": D, "causal": True,
                 "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
                 "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                 "compulsory_bytes": nbytes, "effective_gbs": round(nbytes / ms / 1e6, 1),
