@@ -177,8 +177,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   };
   Item cur = item_at(0);
   if (!cur.valid) return;
-  int N = 0;
-  for (Item it = cur; it.valid; it = item_at(it.k + 1)) N += it.n_tiles;
 
   // ---- Q^T operand of an item: lane holds q[q0w + col][16*ds + 8*half + 0..7].
   // Nothing but the score MFMAs reads it, so a load issued early in a phase
