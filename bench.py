@@ -1,6 +1,6 @@
 """Throughput of the causal attention forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold]
 
 One step is one fa_fwd call (the whole forward pass: causal tile schedule,
 Q/K/V tile loads, both matrix products, online softmax, epilogue with the
@@ -12,6 +12,12 @@ FLOPs follow the chipfoundryservices.com "FlashAttention" reduced-order model
 (outputs.flops_gflop): the two matrix products only, 4*B*H*S^2*D, halved under
 the causal rule.  Bytes are the compulsory ones: Q, K, V read once, O written
 once, the fp32 log-sum-exp written once.
+
+With --cold, each of K further launches is preceded by a 1 GiB write to a
+scratch buffer, which evicts Q, K and V from the L2 caches and the 256 MB
+Infinity Cache, and timed alone with HIP events (the median is reported in
+"cold"): the working set of the smaller workloads otherwise stays cached
+between steps.
 
 The CPU baseline times the fp64 oracle (plain C, all visible cores up to 16) on
 a bounded sample of the same workload -- whole heads, every row -- and checks
@@ -163,6 +169,8 @@ def main():
     ap.add_argument("--variant", default="auto", choices=list(VARIANTS))
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time K launches each after a 1 GiB cache-evicting write (median reported)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run --steps plain device copies of MIB MiB (the "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -258,6 +266,25 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
     }
+    if args.cold:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        times = []
+        for i in range(args.steps):
+            scratch.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        cold_ms = sorted(times)[len(times) // 2]
+        result["cold"] = {"evict_bytes": 1 << 30, "launches": args.steps, "kernel_ms_median": round(cold_ms, 5),
+                          "kernel_ms_min": round(min(times), 5),
+                          "tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2),
+                          "effective_hbm_gbs": round(nbytes / (cold_ms * 1e-3) / 1e9, 1)}
+        log(f"[bench] cold: median {cold_ms:.4f} ms over {args.steps} launches, "
+            f"{result['cold']['effective_hbm_gbs']} GB/s effective")
     if not args.no_cpu_baseline:
         log(f"[bench] oracle on {cpu_heads} whole heads (CPU baseline + parity)")
         base, parity = cpu_baseline(q, k, v, o, lse, cpu_heads, causal, scale)
