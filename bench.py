@@ -1,11 +1,14 @@
 """Throughput of the causal attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold]
+                    [--entry fa_fwd_ws|fa_fwd]
 
-One step is one fa_fwd call (the whole forward pass: causal tile schedule,
+One step is one forward call (the whole forward pass: causal tile schedule,
 Q/K/V tile loads, both matrix products, online softmax, epilogue with the
 log-sum-exp) over one batch of synthetic bf16 input that is already resident in
-HBM.  W untimed steps, then K timed steps between two device synchronisations.
+HBM.  The call is fa_fwd_ws by default: fa_fwd with a scheduling workspace,
+which balances the last work items across XCDs at run time (the same results,
+bit for bit); --entry fa_fwd times the static schedule.  W untimed steps, then K timed steps between two device synchronisations.
 Prints ONE JSON line on stdout; progress goes to stderr.
 
 FLOPs follow the chipfoundryservices.com "FlashAttention" reduced-order model
@@ -169,6 +172,8 @@ def main():
     ap.add_argument("--variant", default="auto", choices=list(VARIANTS))
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--entry", default="fa_fwd_ws", choices=("fa_fwd_ws", "fa_fwd"),
+                    help="the C entry point timed (fa_fwd_ws: with the scheduling workspace)")
     ap.add_argument("--cold", action="store_true",
                     help="also time K launches each after a 1 GiB cache-evicting write (median reported)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -217,9 +222,22 @@ def main():
     if variant == fa.FA_VARIANT_AUTO:
         variant = fa.select_variant(B, H, S, D, fa.FA_DTYPE_BF16)
     stream = torch.cuda.current_stream(dev)
+    use_ws = args.entry == "fa_fwd_ws"
+    if use_ws and args.variant != "auto":
+        raise SystemExit("--entry fa_fwd_ws runs the automatic variant")
+    ws = torch.zeros(fa.fwd_workspace_bytes(), dtype=torch.uint8, device=dev) if use_ws else None
+    # what the library does with the workspace: balance when the ping-pong grid is
+    # resident over whole XCDs with at least 8 heads per XCD
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    n_items = B * H * math.ceil(S / 256)
+    balanced = (use_ws and variant in (fa.FA_VARIANT_MFMA_B256, fa.FA_VARIANT_MFMA_B256_K128)
+                and (B * H) % 8 == 0 and B * H >= 64 and cus % 8 == 0 and n_items > cus)
 
     def step():
-        fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse, variant=variant, stream=stream)
+        if use_ws:
+            fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse, stream=stream, workspace=ws)
+        else:
+            fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse, variant=variant, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -249,7 +267,7 @@ def main():
     traffic = measured_traffic(args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": fa.kernel_name(variant, D, causal), "kernel_ms": round(kernel_ms, 5),
+                "kernel": fa.kernel_name(variant, D, causal, balanced), "kernel_ms": round(kernel_ms, 5),
                 "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
                 "effective_hbm_gbs": round(nbytes / (kernel_ms * 1e-3) / 1e9, 1),
                 "hbm_frac": round(nbytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -263,6 +281,7 @@ def main():
                    "head_dim": D, "causal": causal, "layout": "[B,H,S,D] contiguous",
                    "inputs": f"uniform(-0.8,0.8) seed {args.seed}, scale fp32(1/sqrt({D}))",
                    "variant": [n for n, c in fa.VARIANTS.items() if c == variant][0],
+                   "entry": args.entry, "schedule": "balanced" if balanced else "static",
                    "parallelism": "single GPU"},
         "roofline": roofline,
     }

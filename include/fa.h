@@ -99,6 +99,35 @@ fa_status fa_fwd_variant(const void *q, const void *k, const void *v, void *o, f
                          int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale,
                          fa_dtype dtype, int variant, void *stream);
 
+/*
+ * fa_fwd_ws -- fa_fwd with a scheduling workspace: the same operation, the
+ * same arguments and results, bit for bit.  What the workspace buys: when the
+ * 256-row matrix-core kernel runs resident (more work items than compute
+ * units, B*H a multiple of 8), the last rounds of each XCD's work items
+ * (about an eighth of the work) are not assigned in advance but claimed at
+ * run time through counters in the workspace, and workgroups of an XCD that
+ * runs ahead take items of the others.  Under load each XCD holds its own
+ * clock, so a static split ends with the slowest XCD.  In every other case
+ * the call runs exactly as fa_fwd and the workspace is not touched.
+ *
+ *   workspace  device memory owned by the caller, 4-byte aligned, at least
+ *              fa_fwd_workspace_bytes() bytes, ZERO-FILLED before its first
+ *              use (e.g. one hipMemset).  Every call leaves it zero-filled
+ *              again: its last workgroup resets the counters.  A workspace
+ *              that is not zero when a call starts gives wrong results (work
+ *              items skipped).  Calls that share a workspace must be ordered
+ *              on one stream.
+ *
+ * Returns what fa_fwd returns, and FA_ERR_INVALID_ARGUMENT for a NULL,
+ * misaligned or too small workspace.
+ */
+fa_status fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+                    int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, void *workspace,
+                    int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_fwd_ws needs (a constant, 8192).  Host-only. */
+int64_t fa_fwd_workspace_bytes(void);
+
 /* The variant fa_fwd would run for this shape (an fa_variant value), or -1
  * if the arguments are unsupported.  Host-only; touches no device. */
 int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype);

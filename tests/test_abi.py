@@ -173,3 +173,24 @@ def test_bwd_rejects_before_launch():
     assert _bwd(dtype=fa.FA_DTYPE_FP32) == fa.FA_ERR_UNSUPPORTED                    # bf16 only
     assert _bwd(D=32) == fa.FA_ERR_UNSUPPORTED                                      # D 64 or 128
     assert _bwd(S=1 << 24, D=128) == fa.FA_ERR_UNSUPPORTED                          # S * D >= 2^31
+
+
+def test_fwd_workspace_bytes():
+    """A constant: 8 pool counters, a done count and one slot per workgroup."""
+    assert fa.fwd_workspace_bytes() == 8192
+
+
+def _fwd_ws(ws=P, ws_bytes=8192, ptrs=(P, P, P, P), B=1, H=1, S=64, D=128, scale=0.1, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd_ws_raw(*ptrs, 0, B, H, S, D, True, scale, dtype, ws, ws_bytes)
+
+
+def test_fwd_ws_rejects_before_launch():
+    """fa_fwd_ws checks its workspace, then everything fa_fwd checks; nothing is launched."""
+    assert _fwd_ws(ws=0) == fa.FA_ERR_INVALID_ARGUMENT               # no workspace
+    assert _fwd_ws(ws_bytes=8191) == fa.FA_ERR_INVALID_ARGUMENT      # too small
+    assert _fwd_ws(ws=P + 2) == fa.FA_ERR_INVALID_ARGUMENT           # misaligned
+    assert _fwd_ws(ptrs=(P, P, 0, P)) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _fwd_ws(B=0) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _fwd_ws(scale=float("inf")) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _fwd_ws(D=48) == fa.FA_ERR_UNSUPPORTED
+    assert _fwd_ws(dtype=7) == fa.FA_ERR_UNSUPPORTED

@@ -26,12 +26,12 @@ def test_counters_scaled_by_copy_calibration(tmp_path):
     _write(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", kib)] * 3)
     _write(tmp_path / "f.csv", [
         ("distribution_elementwise_grid_stride_kernel", "FETCH_SIZE", 999.0),  # input generation: ignored
-        ("void fa::pp::attn_fwd_pingpong<128, 128, true>(...)", "FETCH_SIZE", 100.0),
+        ("void fa::pp::attn_fwd_pingpong<128, 128, true, true>(...)", "FETCH_SIZE", 100.0),
         ("void fa::dense::dense_scores<128, true>(...)", "FETCH_SIZE", 10.0),
         ("void fa::dense::dense_softmax<true>(...)", "FETCH_SIZE", 20.0),
         ("void fa::dense::dense_pv<128, true>(...)", "FETCH_SIZE", 30.0)])
     _write(tmp_path / "w.csv", [
-        ("void fa::pp::attn_fwd_pingpong<128, 128, true>(...)", "WRITE_SIZE", 7.0),
+        ("void fa::pp::attn_fwd_pingpong<128, 128, true, true>(...)", "WRITE_SIZE", 7.0),
         ("void fa::dense::dense_scores<128, true>(...)", "WRITE_SIZE", 40.0),
         ("void fa::dense::dense_pv<128, true>(...)", "WRITE_SIZE", 2.0)])
     out = traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
@@ -53,8 +53,8 @@ def test_clock_from_busy_cycles(tmp_path):
     with open(tmp_path / "g.csv", "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=fields)
         w.writeheader()
-        rows = [("void fa::pp::attn_fwd_pingpong<128, 128, true>(...)", 8 * 1.6e6, 1_000_000),
-                ("void fa::pp::attn_fwd_pingpong<128, 128, true>(...)", 8 * 2.0e6, 1_000_000),
+        rows = [("void fa::pp::attn_fwd_pingpong<128, 128, true, true>(...)", 8 * 1.6e6, 1_000_000),
+                ("void fa::pp::attn_fwd_pingpong<128, 128, true, true>(...)", 8 * 2.0e6, 1_000_000),
                 ("void fa::bwd::attn_bwd_dq<128, true, 2>(...)", 8 * 1.0e6, 500_000),
                 ("distribution_elementwise_grid_stride_kernel", 1.0, 10)]
         for i, (name, value, ns) in enumerate(rows):

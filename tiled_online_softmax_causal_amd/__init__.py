@@ -22,7 +22,8 @@ FA_VARIANT_AUTO, FA_VARIANT_MFMA_B256, FA_VARIANT_MFMA_B128, FA_VARIANT_VALU, FA
 VARIANTS = {"auto": 0, "mfma_b256": 1, "mfma_b128": 2, "valu": 3, "mfma_b256_k128": 4}
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_fwd_select_variant", "fa_fwd_tiles_per_head",
+EXPORTS = ("fa_fwd", "fa_fwd_ws", "fa_fwd_workspace_bytes", "fa_fwd_variant", "fa_fwd_select_variant",
+           "fa_fwd_tiles_per_head",
            "fa_dense_fwd", "fa_dense_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_status_str", "fa_last_hip_error", "fa_version")
 
@@ -46,6 +47,10 @@ def load_library(path: str = LIBRARY_PATH):
     p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, p]
     lib.fa_fwd.restype = i32
+    lib.fa_fwd_ws.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, p, i64, p]
+    lib.fa_fwd_ws.restype = i32
+    lib.fa_fwd_workspace_bytes.argtypes = []
+    lib.fa_fwd_workspace_bytes.restype = i64
     lib.fa_fwd_variant.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, i32, p]
     lib.fa_fwd_variant.restype = i32
     lib.fa_fwd_select_variant.argtypes = [i64, i64, i64, i64, i32]
@@ -86,13 +91,15 @@ def tiles_per_head(S: int, causal: bool, variant: int) -> int:
     return load_library().fa_fwd_tiles_per_head(S, int(bool(causal)), variant)
 
 
-def kernel_name(variant: int, D: int, causal: bool) -> str:
-    """Name prefix of the kernel a variant launches (as profilers print it)."""
+def kernel_name(variant: int, D: int, causal: bool, balanced: bool = False) -> str:
+    """Name prefix of the kernel a variant launches (as profilers print it); ``balanced``
+    selects the instance fa_fwd_ws runs when its balanced schedule applies."""
     c = "true" if causal else "false"
+    bal = "true" if balanced else "false"
     if variant == FA_VARIANT_MFMA_B256:
-        return f"fa::pp::attn_fwd_pingpong<{D}, 64, {c}>"
+        return f"fa::pp::attn_fwd_pingpong<{D}, 64, {c}, {bal}>"
     if variant == FA_VARIANT_MFMA_B256_K128:
-        return f"fa::pp::attn_fwd_pingpong<{D}, 128, {c}>"
+        return f"fa::pp::attn_fwd_pingpong<{D}, 128, {c}, {bal}>"
     if variant == FA_VARIANT_MFMA_B128:
         return f"fa::attn_fwd_mfma_bf16<{D}, 1, {c}>"
     if variant == FA_VARIANT_VALU:
@@ -110,6 +117,21 @@ def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: 
                               int(variant), stream or None)
 
 
+def fa_fwd_ws_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, S: int,
+                  D: int, causal: bool, scale: float, dtype: int, ws_ptr: int, ws_bytes: int,
+                  stream: int = 0) -> int:
+    """Call fa_fwd_ws with raw device addresses; returns the fa_status code."""
+    lib = load_library()
+    return lib.fa_fwd_ws(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None, lse_ptr or None,
+                         B, H, S, D, int(bool(causal)), float(scale), dtype, ws_ptr or None, ws_bytes,
+                         stream or None)
+
+
+def fwd_workspace_bytes() -> int:
+    """Bytes of the scheduling workspace fa_fwd_ws takes."""
+    return load_library().fa_fwd_workspace_bytes()
+
+
 def _check(status: int):
     if status == FA_OK:
         return
@@ -123,13 +145,16 @@ def _check(status: int):
 
 
 def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
-        return_lse: bool = True, variant="auto", stream=None):
+        return_lse: bool = True, variant="auto", stream=None, workspace=None):
     """Attention forward on ``[B, H, S, D]`` CUDA tensors (bf16 or fp32).
 
     Returns ``(o, lse)`` -- ``o`` like ``q``, ``lse`` fp32 ``[B, H, S]`` (natural
     log of the softmax denominator, scale included) -- or ``o`` alone when
     ``return_lse`` is false.  ``scale`` defaults to ``1/sqrt(D)``.  The work is
-    enqueued on ``stream`` (default: torch's current stream).
+    enqueued on ``stream`` (default: torch's current stream).  With a
+    ``workspace`` (a device tensor of at least ``fwd_workspace_bytes()``
+    bytes) the call goes through fa_fwd_ws (run-time balancing of the last
+    work items across XCDs; the same results), and ``variant`` must be auto.
     """
     import torch
 
@@ -162,9 +187,18 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
         stream = torch.cuda.current_stream(q.device)
     st = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(q.device):
-        status = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr() if lse is not None else 0, B, H, S, D, causal, scale,
-                            dtype, st, variant)
+        if workspace is not None:
+            if variant != FA_VARIANT_AUTO:
+                raise ValueError("a workspace call runs the automatic variant")
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous device tensor")
+            status = fa_fwd_ws_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else 0, B, H, S, D, causal, scale,
+                                   dtype, workspace.data_ptr(), workspace.numel() * workspace.element_size(), st)
+        else:
+            status = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else 0, B, H, S, D, causal, scale,
+                                dtype, st, variant)
     _check(status)
     return (out, lse) if return_lse else out
 

@@ -94,25 +94,41 @@ int device_cus() {
 // The ping-pong kernel holds a whole CU (LDS), so with more work items than
 // CUs it runs resident: one workgroup per CU walking its items, instead of a
 // grid of one workgroup per item that the dispatcher refills as they finish.
+// With a schedule workspace (sched) and heads grouped per XCD, the resident
+// grid balances the last part of its work across XCDs (the balanced schedule
+// in fa_fwd_pingpong.h); otherwise the schedule is static.
 template <int D, int BK>
 hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
-                           int64_t S, int causal, float scale, hipStream_t stream) {
+                           int64_t S, int causal, float scale, unsigned* sched, hipStream_t stream) {
   const int64_t n_qb = ceil_div(S, fa::pp::kBQ);
   const int64_t n_items = BH * n_qb;
   const int cus = device_cus();
   const int64_t grid = cus >= 8 && n_items > cus ? cus : n_items;
   const int xcd_group = (BH % kNumXcd) == 0;
+  // balanced: a resident grid over whole XCDs with at least 8 heads per XCD
+  const bool balanced = sched && xcd_group && grid < n_items && grid % kNumXcd == 0 &&
+                        grid <= fa::pp::kSchedMaxGrid && BH >= 8 * kNumXcd;
   const float c = scale * kLog2e;  // the kernel takes a scale of either sign
   const auto* Q = static_cast<const uint16_t*>(q);
   const auto* K = static_cast<const uint16_t*>(k);
   const auto* V = static_cast<const uint16_t*>(v);
   auto* O = static_cast<uint16_t*>(o);
-  if (causal)
-    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
-                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)n_items, c, xcd_group);
-  else
-    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false>), dim3((unsigned)grid), dim3(fa::pp::kThreads), 0,
-                       stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)n_items, c, xcd_group);
+  const dim3 g((unsigned)grid), b(fa::pp::kThreads);
+  const int s = (int)S, nq = (int)n_qb, ni = (int)n_items;
+  if (balanced) {
+    if (causal)
+      hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true, true>), g, b, 0, stream, Q, K, V, O, lse, s, nq, ni,
+                         c, xcd_group, sched);
+    else
+      hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false, true>), g, b, 0, stream, Q, K, V, O, lse, s, nq, ni,
+                         c, xcd_group, sched);
+  } else if (causal) {
+    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true, false>), g, b, 0, stream, Q, K, V, O, lse, s, nq, ni,
+                       c, xcd_group, nullptr);
+  } else {
+    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false, false>), g, b, 0, stream, Q, K, V, O, lse, s, nq, ni,
+                       c, xcd_group, nullptr);
+  }
   return hipGetLastError();
 }
 
@@ -219,9 +235,14 @@ int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant) {
   return tiles;
 }
 
-fa_status fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                         int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, int variant,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward with a given variant; sched is the balanced schedule's workspace or NULL.
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, int variant, unsigned* sched,
+                   void* stream) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARGUMENT;
   if (B < 1 || H < 1 || S < 1 || D < 1) return FA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
@@ -243,11 +264,11 @@ fa_status fa_fwd_variant(const void* q, const void* k, const void* v, void* o, f
     err = dtype == FA_DTYPE_FP32 ? launch_valu_d<float>(q, k, v, o, lse, BH, S, D, causal, scale, st)
                                  : launch_valu_d<uint16_t>(q, k, v, o, lse, BH, S, D, causal, scale, st);
   } else if (variant == FA_VARIANT_MFMA_B256_K128) {
-    err = D == 128 ? launch_pingpong<128, 128>(q, k, v, o, lse, BH, S, causal, scale, st)
-                   : launch_pingpong<64, 128>(q, k, v, o, lse, BH, S, causal, scale, st);
+    err = D == 128 ? launch_pingpong<128, 128>(q, k, v, o, lse, BH, S, causal, scale, sched, st)
+                   : launch_pingpong<64, 128>(q, k, v, o, lse, BH, S, causal, scale, sched, st);
   } else if (variant == FA_VARIANT_MFMA_B256) {
-    err = D == 128 ? launch_pingpong<128, 64>(q, k, v, o, lse, BH, S, causal, scale, st)
-                   : launch_pingpong<64, 64>(q, k, v, o, lse, BH, S, causal, scale, st);
+    err = D == 128 ? launch_pingpong<128, 64>(q, k, v, o, lse, BH, S, causal, scale, sched, st)
+                   : launch_pingpong<64, 64>(q, k, v, o, lse, BH, S, causal, scale, sched, st);
   } else {
     err = D == 128 ? launch_mfma<128, 1>(q, k, v, o, lse, BH, S, causal, scale, st)
                    : launch_mfma<64, 1>(q, k, v, o, lse, BH, S, causal, scale, st);
@@ -259,9 +280,29 @@ fa_status fa_fwd_variant(const void* q, const void* k, const void* v, void* o, f
   return FA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                         int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, int variant,
+                         void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, variant, nullptr, stream);
+}
+
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                  int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, void* stream) {
-  return fa_fwd_variant(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, FA_VARIANT_AUTO, stream);
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, FA_VARIANT_AUTO, nullptr, stream);
+}
+
+int64_t fa_fwd_workspace_bytes(void) { return fa::pp::kSchedBytes; }
+
+fa_status fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                    int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, void* workspace,
+                    int64_t workspace_bytes, void* stream) {
+  if (!workspace || !aligned(workspace, 4) || workspace_bytes < fa::pp::kSchedBytes) return FA_ERR_INVALID_ARGUMENT;
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, FA_VARIANT_AUTO,
+                  static_cast<unsigned*>(workspace), stream);
 }
 
 int64_t fa_dense_workspace_bytes(int64_t S) { return S < 1 ? 0 : fa::dense::head_bytes(S); }

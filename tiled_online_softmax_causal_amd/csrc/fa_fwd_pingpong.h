@@ -85,6 +85,13 @@ constexpr int kQW = 32;                 // query rows per wave
 constexpr int kBQ = kQW * kWaves;       // query rows per workgroup
 constexpr int kAhead = 5;               // MFMAs between an operand's LDS read and its use
 constexpr float kOverflowSum = 0x1p64f; // a tile sum above this redoes the tile with the exact maximum
+// Balanced schedule's workspace (32-bit words): 8 pool counters 128 bytes apart
+// (words 0, 32, ..., 224), a count of finished workgroups (word 256), then one
+// 8-byte broadcast slot per workgroup from word 288.  It is zero between calls.
+constexpr int kSchedBytes = 8192;
+constexpr int kSchedDone = 256;
+constexpr int kSchedSlots = 288;
+constexpr int kSchedMaxGrid = (kSchedBytes / 4 - kSchedSlots) / 2;
 
 // LDS tiles are row-major, D*2 bytes per row, with the 16-byte chunks of each
 // row XOR-swizzled by swz(row) (masked to the row's chunk count).  For d = 128
@@ -133,11 +140,11 @@ __device__ __forceinline__ void schedule_matrix_phase(std::integer_sequence<int,
   (schedule_item<NPV, N, I>(), ...);
 }
 
-template <int D, int BK, bool CAUSAL>
+template <int D, int BK, bool CAUSAL, bool BALANCED>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int S, int n_qb, int n_items, float c_log2,
-    int xcd_group) {
+    int xcd_group, unsigned* __restrict__ sched) {
   using G = Geo<D, BK>;
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -153,6 +160,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
+  // the lane's index recomputed from the hardware, so that no thread index is
+  // held in a register through the whole kernel
+  auto lane_id = []() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); };
   const int grp = wave >> 2;   // 0: matrix phase first, carries K; 1: one phase behind, carries V
   const int col = lane & 31;   // the query this lane owns, within the wave
   const int half = lane >> 5;  // which key half of each 32-key block
@@ -169,395 +179,500 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     int bh, qb, n_tiles, k;
     bool valid;
   };
-  auto item_at = [&](int k) -> Item {
-    int b = 0, q = 0;
-    if (!next_item(blockIdx.x, k, gridDim.x, n_qb, n_items, xcd_group, b, q)) return Item{0, 0, 1, k, false};
+  //
+  // Balanced schedule (a resident grid of G = 8P workgroups, heads grouped per
+  // XCD, at least 8 heads per XCD).  Each XCD runs at its own clock under load,
+  // and a static schedule ends with the slowest XCD.  So the last eighth of
+  // every XCD's heads (hp of its hx heads) form a pool instead of being
+  // scheduled in advance.  A workgroup that has finished its static items
+  // claims pool items one at a time with an atomic counter per XCD: first its
+  // own XCD's pool, then the other XCDs'.  A pool hands out its items heaviest
+  // first across its heads (every head's last query block, then the one
+  // before, ...), so that the last claims are the shortest items.  Each
+  // claimed item runs as a pipeline of its own.  Which workgroup computes an
+  // item does not change its arithmetic, so the outputs equal the static
+  // schedule's bit for bit.
+  // sched: 8 counters 128 bytes apart, a done count, then one (bh, qb) slot per
+  // workgroup.  The counters start at zero, and the last workgroup to finish
+  // zeroes them again for the next call.
+  const int hx = n_items / (8 * n_qb);           // heads per XCD
+  const int hp = BALANCED ? max(1, hx / 8) : 0;  // of them in the pool
+  const int pool_base = (hx - hp) * n_qb;        // the XCD's static items come before it
+  auto make_item = [&](int b, int q, int k) -> Item {
     const int kv_end = CAUSAL ? min(S, q * kBQ + kBQ) : S;
     return Item{b, q, (kv_end + BK - 1) / BK, k, true};
   };
-  Item cur = item_at(0);
-  if (!cur.valid) return;
-
-  // ---- Q^T operand of an item: lane holds q[q0w + col][16*ds + 8*half + 0..7].
-  // Nothing but the score MFMAs reads it, so a load issued early in a phase
-  // is waited for only where those MFMAs need it.
-  bf16x8_t qreg[DS];
-  auto load_q = [&](const Item& it) {
-    const int qrow = min(it.qb * kBQ + wave * kQW + col, S - 1);
-    const uint16_t* src = Q + (size_t)it.bh * S * D + (size_t)qrow * D + 8 * half;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qreg[ds] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ds);
+  // the k-th item of this workgroup's static list: in the balanced schedule
+  // the snake order over the XCD's items in front of its pool
+  auto static_item = [&](int k) -> Item {
+    int b = 0, q = 0;
+    if constexpr (BALANCED) {
+      const int p = (int)gridDim.x >> 3, j = blockIdx.x >> 3;
+      const int idx = p * k + ((k & 1) ? p - 1 - j : j);
+      if (idx >= pool_base) return Item{0, 0, 1, k, false};
+      b = (idx / n_qb) * 8 + (blockIdx.x & 7);
+      q = n_qb - 1 - idx % n_qb;
+    } else if (!next_item(blockIdx.x, k, gridDim.x, n_qb, n_items, xcd_group, b, q)) {
+      return Item{0, 0, 1, k, false};
+    }
+    return make_item(b, q, k);
   };
-  load_q(cur);
-
-  f32x16_t oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
-  // Scores and probabilities share registers: the bf16 probabilities of
-  // k-step ks (keys 16*ks.., 8 per lane) are written over the first four of
-  // the eight fp32 scores they come from, sacc[ks/2][8*(ks%2) + 0..3], and are
-  // read from there as the B operand of the P.V MFMA before the next score
-  // MFMAs overwrite the accumulator.
-  f32x16_t sacc[KB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) sacc[kb] = (f32x16_t){};
-  auto p_operand = [&](int ks) {
-    const f32x16_t& a = sacc[ks >> 1];
-    const int r0 = 8 * (ks & 1);
-    const f32x4_t w = {a[r0], a[r0 + 1], a[r0 + 2], a[r0 + 3]};
-    return __builtin_bit_cast(bf16x8_t, w);
-  };
-  auto set_p = [&](int ks, bf16x8_t p8) {
-    const f32x4_t w = __builtin_bit_cast(f32x4_t, p8);
-    const int r0 = 8 * (ks & 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sacc[ks >> 1][r0 + j] = w[j];
-  };
-  float m_run = -__builtin_inff(), l_run = 0.f;
-
-  // ---- staging: HBM -> LDS directly (global_load_lds, 16 bytes per lane).
-  // Thread gtid of the carrying group fills 16-byte slots gtid, gtid + 256, ...
-  // (row-major) of its tensor's tile; the source is the logical chunk that the
-  // swizzle puts in that slot.  Rows past the end of the sequence re-read row
-  // S-1 (their scores are masked).  K tile T lives in K slot T % 3, V tile T
-  // in V slot T % 2.
-  const int gtid = tid & (kGroupThreads - 1);
-  const int gwave = wave & 3;
-  const int g_row = gtid / G::kChunks;
-  const int g_lch = (gtid % G::kChunks) ^ swz<G::kChunks>(g_row);  // same for every load step
-  char* const kbuf0 = lds;
-  char* const vbuf0 = lds + G::kStagesK * G::kTileBytes;
-  auto kslot = [](int T) { return (T + G::kStagesK) % G::kStagesK; };
-  auto vslot = [](int T) { return (T + G::kStagesV) % G::kStagesV; };
-  // One tile copy: source tile (wave-uniform base), its rows left before the
-  // end of the sequence, and the ring slot.  A null tile means no copy.
-  struct Copy {
-    const uint16_t* tile;
-    int rows;
-    char* slot;
-  };
-  // The copy cursor walks this group's tensor along the tile sequence; past
-  // its end it keeps re-reading the last tile into the next slots, which keeps
-  // the wait counts uniform.
-  Item c_it = cur;
-  int c_t = 0, c_T = 0;
-  auto next_copy = [&]() -> Copy {
-    const Copy c{(grp == 0 ? K : V) + (size_t)c_it.bh * S * D + (size_t)c_t * BK * D, S - c_t * BK,
-                 grp == 0 ? kbuf0 + kslot(c_T) * G::kTileBytes : vbuf0 + vslot(c_T) * G::kTileBytes};
-    ++c_T;
-    if (c_t + 1 < c_it.n_tiles) {
-      ++c_t;
-    } else {
-      const Item nx = item_at(c_it.k + 1);
-      if (nx.valid) {
-        c_it = nx;
-        c_t = 0;
+  // The next pool item for this workgroup (-1 when every pool is empty).  One
+  // thread takes it from the counters and writes it to the workgroup's slot;
+  // the barriers around it make every wave finish the previous segment first
+  // and read the slot after the write has completed.
+  auto claim = [&]() -> Item {
+    unsigned* const slot = sched + kSchedSlots + 2 * blockIdx.x;
+    phase_barrier();
+    if (wave == 0 && lane_id() == 0) {
+      const int x = blockIdx.x & 7;
+      int b = -1, q = 0;
+      for (int d = 0; d < 8 && b < 0; ++d) {
+        const int y = (x + d) & 7;
+        const unsigned i = __hip_atomic_fetch_add(&sched[32 * y], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (i < (unsigned)(hp * n_qb)) {  // pool position i: weight rank i / hp of pool head i % hp
+          b = (hx - hp + (int)i % hp) * 8 + y;
+          q = n_qb - 1 - (int)i / hp;
+        }
       }
+      __hip_atomic_store(slot, (unsigned)b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot + 1, (unsigned)q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
     }
-    return c;
+    phase_barrier();
+    const int b = __builtin_amdgcn_readfirstlane((int)__hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const int q = __builtin_amdgcn_readfirstlane((int)__hip_atomic_load(slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return b < 0 ? Item{0, 0, 1, 0, false} : make_item(b, q, 0);
   };
-  // load step i of a copy: a 32-bit per-lane byte offset from the tile base;
-  // rows clamp to the sequence's last row (comparing whole offsets keeps the
-  // lane's chunk)
-  const unsigned g_off = (unsigned)(g_row * G::kRowBytes + g_lch * 16);
-  auto copy_step = [&](int i, const Copy& c, unsigned off0) {
-    const unsigned lim = (unsigned)((c.rows - 1) * G::kRowBytes + g_lch * 16);
-    const unsigned voff = min(off0 + (unsigned)(i * G::kRowsPerLoad * G::kRowBytes), lim);
-    copy16_to_lds(c.tile, voff, c.slot + (i * kGroupThreads + gwave * 64) * 16);
-  };
-  // per-lane read offsets within a tile.  K: row 32*kb + col, logical chunk
-  // 2*ds + half.  V (transposed read): rows 16*ks + 4*half + u/4 (+8 for the
-  // upper k-slots), logical chunk 4*db + 2*(quad%2) + (u%4)/2, byte 8*(u%2).
-  int k_off[DS], v_off_lo[DB], v_off_hi[DB];
-  {
-    const int sk = swz<G::kChunks>(col);
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) k_off[ds] = col * G::kRowBytes + (((2 * ds + half) ^ sk) << 4);
-    const int vr = 4 * half + (u >> 2);
-    const int s_lo = swz<G::kChunks>(vr), s_hi = swz<G::kChunks>(vr + 8);
-    const int c_l = 2 * (quad & 1) + ((u & 3) >> 1);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      v_off_lo[db] = vr * G::kRowBytes + (((4 * db + c_l) ^ s_lo) << 4) + 8 * (u & 1);
-      v_off_hi[db] = (vr + 8) * G::kRowBytes + (((4 * db + c_l) ^ s_hi) << 4) + 8 * (u & 1);
-    }
-  }
-
-  // ---- matrix phase T: O^T += V_{T-1}^T P_{T-1}^T (DB accumulators, k-step
-  // outer), then S_T^T = K_T Q^T (KB accumulators, alternating).
-  auto matrix_phase = [&](int T) {
-    constexpr int NPV = DB * KS, NSC = DS * KB, NM = NPV + NSC;
-    // slot bases as opaque wave-uniform values: the compiler would otherwise
-    // strength-reduce T % 3 into one induction register per read address
-    const char* Vl = vbuf0 + __builtin_amdgcn_readfirstlane(vslot(T - 1) * G::kTileBytes);
-    const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(T) * G::kTileBytes);
-    // the matrix-core wave issues first; the softmax wave on the same SIMD
-    // fills the issue slots the MFMAs leave free
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      if (i < NPV) {
-        const int ks = i / DB, db = i % DB;
-        const char* vp = Vl + 16 * ks * G::kRowBytes;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + v_off_lo[db]));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + v_off_hi[db]));
-        const bf16x8_t av = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
-                                                    __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p_operand(ks), oacc[db], 0, 0, 0);
+  // One segment: the pipeline over an item list from its first item `first`:
+  // the static list, or (SINGLE) one claimed item.  The static schedule runs
+  // one segment; the balanced one runs the static part, then one segment per
+  // claimed item.
+  auto run_segment = [&](const Item first, auto single_c) {
+    constexpr bool SINGLE = decltype(single_c)::value;
+    auto item_at = [&](int k) -> Item {
+      if constexpr (SINGLE) {
+        // opaque at every use, so that nothing derived from the one item is
+        // hoisted out of the tile loop into registers held through it
+        int bh = first.bh, qb = first.qb, nt = first.n_tiles;
+        asm volatile("" : "+s"(bh), "+s"(qb), "+s"(nt));
+        return k == 0 ? Item{bh, qb, nt, 0, true} : Item{0, 0, 1, k, false};
       } else {
-        const int j = i - NPV, ds = j / KB, kb = j % KB;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
+        return static_item(k);
       }
-    }
-    schedule_matrix_phase<NPV, NM>(std::make_integer_sequence<int, NM>{});
-    __builtin_amdgcn_s_setprio(0);
-  };
-  // Every matrix phase runs the same full body, which keeps the loop's
-  // register allocation simple.  Where a product is not needed its result is
-  // harmless: in phase 0 the probabilities are zero and the V ring slot read
-  // was zero-filled, and for a tile a wave does not see (past its rows'
-  // diagonal) its softmax phase zeroes the probabilities, so the P.V product
-  // adds exactly 0; the scores of phase N (past the last tile) are never used.
+    };
+    Item cur = first;
+    // The lane's indices, made opaque per segment: the offsets derived from
+    // them are then formed in each segment instead of being shared by all
+    // segments and held in registers through the static one.
+    int tid_s = wave * 64 + lane_id();
+    asm volatile("" : "+v"(tid_s));
+    const int lane = tid_s & 63, col = lane & 31, half = lane >> 5, u = lane & 15, quad = lane >> 4;
 
-  // ---- epilogue of an item: O = acc / l (bf16, round to nearest even),
-  // lse = ln2 * (m + log2 l); then the state starts over for the next item.
-  // In the accumulator layout lanes l and l^32 hold the two 8-byte halves of
-  // each 16-byte piece of one row; one v_permlane32_swap per dword hands each
-  // lane a whole piece of its own and its partner's, so every store writes 32
-  // contiguous bytes of each of 32 rows (8 stores instead of 16 of 16 bytes).
-  auto finish_item = [&](const Item& it) {
-    const int qi = it.qb * kBQ + wave * kQW + col;
-    const float l_tot = sum_halves(l_run);
-    const float inv = 1.0f / l_tot;  // rows past S (l = 0) are not stored
-    uint16_t* const orow = O + (size_t)it.bh * S * D + (size_t)min(qi, S - 1) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; rg += 2) {
-        const f32x4_t v0 = {oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv,
-                            oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv};
-        const f32x4_t v1 = {oacc[db][4 * rg + 4] * inv, oacc[db][4 * rg + 5] * inv,
-                            oacc[db][4 * rg + 6] * inv, oacc[db][4 * rg + 7] * inv};
-        // a0: columns 32db + 8rg + 4half + 0..3, a1: the same for rg + 1
-        const u32x2_t a0 = __builtin_bit_cast(u32x2_t, __builtin_convertvector(v0, bf16x4_t));
-        const u32x2_t a1 = __builtin_bit_cast(u32x2_t, __builtin_convertvector(v1, bf16x4_t));
-        // the lower half-wave keeps piece rg and needs its partner's a0; the
-        // upper keeps piece rg + 1 and needs its partner's a1
-        u32x2_t got;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const unsigned send = half ? a0[e] : a1[e];
-          const auto p = __builtin_amdgcn_permlane32_swap(send, send, false, false);
-          got[e] = half ? p[0] : p[1];
-        }
-        const u32x4_t piece = half ? (u32x4_t){got[0], got[1], a1[0], a1[1]} : (u32x4_t){a0[0], a0[1], got[0], got[1]};
-        if (qi < S) *reinterpret_cast<u32x4_t*>(orow + 32 * db + 8 * (rg + half)) = piece;
-      }
-    if (LSE && half == 0 && qi < S) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * common::kLn2;
-#pragma unroll
+    // ---- Q^T operand of an item: lane holds q[q0w + col][16*ds + 8*half + 0..7].
+    // Nothing but the score MFMAs reads it, so a load issued early in a phase
+    // is waited for only where those MFMAs need it.
+    bf16x8_t qreg[DS];
+    auto load_q = [&](const Item& it) {
+      const int qrow = min(it.qb * kBQ + wave * kQW + col, S - 1);
+      const uint16_t* src = Q + (size_t)it.bh * S * D + (size_t)qrow * D + 8 * half;
+  #pragma unroll
+      for (int ds = 0; ds < DS; ++ds) qreg[ds] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ds);
+    };
+    load_q(cur);
+
+    f32x16_t oacc[DB];
+  #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
-    m_run = -__builtin_inff();
-    l_run = 0.f;
-  };
+    // Scores and probabilities share registers: the bf16 probabilities of
+    // k-step ks (keys 16*ks.., 8 per lane) are written over the first four of
+    // the eight fp32 scores they come from, sacc[ks/2][8*(ks%2) + 0..3], and are
+    // read from there as the B operand of the P.V MFMA before the next score
+    // MFMAs overwrite the accumulator.
+    f32x16_t sacc[KB];
+  #pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = (f32x16_t){};
+    auto p_operand = [&](int ks) {
+      const f32x16_t& a = sacc[ks >> 1];
+      const int r0 = 8 * (ks & 1);
+      const f32x4_t w = {a[r0], a[r0 + 1], a[r0 + 2], a[r0 + 3]};
+      return __builtin_bit_cast(bf16x8_t, w);
+    };
+    auto set_p = [&](int ks, bf16x8_t p8) {
+      const f32x4_t w = __builtin_bit_cast(f32x4_t, p8);
+      const int r0 = 8 * (ks & 1);
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) sacc[ks >> 1][r0 + j] = w[j];
+    };
+    float m_run = -__builtin_inff(), l_run = 0.f;
 
-  // ---- softmax phase for tile t of item `it` (flattened index T): S -> bf16
-  // P, running max / sum.  The NL load steps of copy cp are issued along the
-  // way, one per KS / NL exponential steps (pinned there by a scheduling
-  // barrier).  When `next_q` is set the next item's Q operand has already been
-  // loaded over this item's (its latency hidden by this phase), and the rare
-  // recompute below reloads this item's first.
-  auto softmax_phase = [&](const Item& it, int t, int T, const Copy& cp, bool next_q, const Item& nx) {
-    const int q0w = it.qb * kBQ + wave * kQW;
-    // tiles this wave takes part in (its rows see keys below min(S, q0w + 32))
-    const int n_w = q0w >= S ? 0 : (CAUSAL ? min(it.n_tiles, (min(q0w + kQW, S) - 1) / BK + 1) : it.n_tiles);
-    // the copy offsets are formed here, not hoisted out of the loop, where
-    // they would hold registers through the matrix phase
-    unsigned off0 = g_off;
-    asm volatile("" : "+v"(off0));
-    auto copy_at = [&](int ks) {
-      if (ks % (KS / NL) == 0) {
-        copy_step(ks / (KS / NL), cp, off0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    // ---- staging: HBM -> LDS directly (global_load_lds, 16 bytes per lane).
+    // Thread gtid of the carrying group fills 16-byte slots gtid, gtid + 256, ...
+    // (row-major) of its tensor's tile; the source is the logical chunk that the
+    // swizzle puts in that slot.  Rows past the end of the sequence re-read row
+    // S-1 (their scores are masked).  K tile T lives in K slot T % 3, V tile T
+    // in V slot T % 2.
+    const int gtid = tid_s & (kGroupThreads - 1);
+    const int gwave = wave & 3;
+    const int g_row = gtid / G::kChunks;
+    const int g_lch = (gtid % G::kChunks) ^ swz<G::kChunks>(g_row);  // same for every load step
+    char* const kbuf0 = lds;
+    char* const vbuf0 = lds + G::kStagesK * G::kTileBytes;
+    auto kslot = [](int T) { return (T + G::kStagesK) % G::kStagesK; };
+    auto vslot = [](int T) { return (T + G::kStagesV) % G::kStagesV; };
+    // One tile copy: source tile (wave-uniform base), its rows left before the
+    // end of the sequence, and the ring slot.  A null tile means no copy.
+    struct Copy {
+      const uint16_t* tile;
+      int rows;
+      char* slot;
     };
-    if (t >= n_w) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) set_p(ks, (bf16x8_t){});
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) copy_at(ks);
-      return;
+    // The copy cursor walks this group's tensor along the tile sequence; past
+    // its end it keeps re-reading the last tile into the next slots, which keeps
+    // the wait counts uniform.
+    Item c_it = cur;
+    int c_t = 0, c_T = 0;
+    auto next_copy = [&]() -> Copy {
+      const Copy c{(grp == 0 ? K : V) + (size_t)c_it.bh * S * D + (size_t)c_t * BK * D, S - c_t * BK,
+                   grp == 0 ? kbuf0 + kslot(c_T) * G::kTileBytes : vbuf0 + vslot(c_T) * G::kTileBytes};
+      ++c_T;
+      if (c_t + 1 < c_it.n_tiles) {
+        ++c_t;
+      } else {
+        const Item nx = item_at(c_it.k + 1);
+        if (nx.valid) {
+          c_it = nx;
+          c_t = 0;
+        }
+      }
+      return c;
+    };
+    // load step i of a copy: a 32-bit per-lane byte offset from the tile base;
+    // rows clamp to the sequence's last row (comparing whole offsets keeps the
+    // lane's chunk)
+    const unsigned g_off = (unsigned)(g_row * G::kRowBytes + g_lch * 16);
+    auto copy_step = [&](int i, const Copy& c, unsigned off0) {
+      const unsigned lim = (unsigned)((c.rows - 1) * G::kRowBytes + g_lch * 16);
+      const unsigned voff = min(off0 + (unsigned)(i * G::kRowsPerLoad * G::kRowBytes), lim);
+      copy16_to_lds(c.tile, voff, c.slot + (i * kGroupThreads + gwave * 64) * 16);
+    };
+    // per-lane read offsets within a tile.  K: row 32*kb + col, logical chunk
+    // 2*ds + half.  V (transposed read): rows 16*ks + 4*half + u/4 (+8 for the
+    // upper k-slots), logical chunk 4*db + 2*(quad%2) + (u%4)/2, byte 8*(u%2).
+    int k_off[DS], v_off_lo[DB], v_off_hi[DB];
+    {
+      const int sk = swz<G::kChunks>(col);
+  #pragma unroll
+      for (int ds = 0; ds < DS; ++ds) k_off[ds] = col * G::kRowBytes + (((2 * ds + half) ^ sk) << 4);
+      const int vr = 4 * half + (u >> 2);
+      const int s_lo = swz<G::kChunks>(vr), s_hi = swz<G::kChunks>(vr + 8);
+      const int c_l = 2 * (quad & 1) + ((u & 3) >> 1);
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        v_off_lo[db] = vr * G::kRowBytes + (((4 * db + c_l) ^ s_lo) << 4) + 8 * (u & 1);
+        v_off_hi[db] = (vr + 8) * G::kRowBytes + (((4 * db + c_l) ^ s_hi) << 4) + 8 * (u & 1);
+      }
     }
-    const int kv0 = t * BK;
-    const int qi = q0w + col;
-    // Tiles that straddle the diagonal or run past S move to the base-2 domain
-    // here, so a hidden score is a plain -inf even when the scale is 0.
-    const bool masked = (CAUSAL && kv0 + BK - 1 > q0w) || kv0 + BK > S;
-    const float c_t = masked ? 1.f : c_log2;
-    auto apply_mask = [&]() {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kj = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool hidden = (CAUSAL && kj > qi) || kj >= S;
-          sacc[kb][r] = hidden ? -__builtin_inff() : sacc[kb][r] * c_log2;
-        }
-    };
-    if (masked) apply_mask();
-    // exponentiate against the running maximum (the copies interleaved when
-    // COPIES); rs is the lane's share of the tile's row sum
-    float rs = 0.f;
-    auto exponentiate = [&](auto copies_c) {
-      constexpr bool COPIES = decltype(copies_c)::value;
-      const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
-      rs = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int kb = ks >> 1, r0 = 8 * (ks & 1);
-        bf16x8_t p8;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const f32x2_t x = {__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e], c_t, neg_m)),
-                             __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e + 1], c_t, neg_m))};
-          rs += x[0];
-          rs += x[1];
-          const bf16x2_t b = __builtin_convertvector(x, bf16x2_t);
-          p8[e] = b[0];
-          p8[e + 1] = b[1];
-        }
-        set_p(ks, p8);
-        if constexpr (COPIES) copy_at(ks);
-      }
-    };
-    // The first tile sets the running maximum exactly.  Later tiles
-    // exponentiate against it at once; only if some row's tile sum then passes
-    // 2^64 (a score about 58 above the running maximum, base 2) is the tile
-    // redone: its scores, which the probabilities have overwritten, are
-    // recomputed from K_T (still in its LDS slot: K_{T+3} is copied two phases
-    // later), the maximum is taken exactly, and O and l are rescaled.
-    // (the maximum of the scaled scores: the scale may be negative)
-    auto take_exact_max = [&]() {
-      float mxk[KB];  // one three-input max chain per 32-key block
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        mxk[kb] = fmaxf(sacc[kb][0] * c_t, sacc[kb][1] * c_t);
-#pragma unroll
-        for (int r = 2; r < 16; r += 2) mxk[kb] = max3(mxk[kb], sacc[kb][r] * c_t, sacc[kb][r + 1] * c_t);
-      }
-      float mx = mxk[0];
-#pragma unroll
-      for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mxk[kb]);
-      const float m_new = fmaxf(m_run, max_halves(mx));
-      const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-    };
-    if (t == 0) take_exact_max();
-    exponentiate(T_{});
-    if (t > 0 && __builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
-      if (next_q) load_q(it);
+
+    // ---- matrix phase T: O^T += V_{T-1}^T P_{T-1}^T (DB accumulators, k-step
+    // outer), then S_T^T = K_T Q^T (KB accumulators, alternating).
+    auto matrix_phase = [&](int T) {
+      constexpr int NPV = DB * KS, NSC = DS * KB, NM = NPV + NSC;
+      // slot bases as opaque wave-uniform values: the compiler would otherwise
+      // strength-reduce T % 3 into one induction register per read address
+      const char* Vl = vbuf0 + __builtin_amdgcn_readfirstlane(vslot(T - 1) * G::kTileBytes);
       const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(T) * G::kTileBytes);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
+      // the matrix-core wave issues first; the softmax wave on the same SIMD
+      // fills the issue slots the MFMAs leave free
+      __builtin_amdgcn_s_setprio(1);
+  #pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        if (i < NPV) {
+          const int ks = i / DB, db = i % DB;
+          const char* vp = Vl + 16 * ks * G::kRowBytes;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + v_off_lo[db]));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + v_off_hi[db]));
+          const bf16x8_t av = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo),
+                                                      __builtin_bit_cast(bf16x4_t, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p_operand(ks), oacc[db], 0, 0, 0);
+        } else {
+          const int j = i - NPV, ds = j / KB, kb = j % KB;
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);  // one operand read at a time: this path is rare
         }
-      if (next_q) load_q(nx);
+      }
+      schedule_matrix_phase<NPV, NM>(std::make_integer_sequence<int, NM>{});
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // Every matrix phase runs the same full body, which keeps the loop's
+    // register allocation simple.  Where a product is not needed its result is
+    // harmless: in phase 0 the probabilities are zero and the V ring slot read
+    // was zero-filled, and for a tile a wave does not see (past its rows'
+    // diagonal) its softmax phase zeroes the probabilities, so the P.V product
+    // adds exactly 0; the scores of phase N (past the last tile) are never used.
+
+    // ---- epilogue of an item: O = acc / l (bf16, round to nearest even),
+    // lse = ln2 * (m + log2 l); then the state starts over for the next item.
+    // In the accumulator layout lanes l and l^32 hold the two 8-byte halves of
+    // each 16-byte piece of one row; one v_permlane32_swap per dword hands each
+    // lane a whole piece of its own and its partner's, so every store writes 32
+    // contiguous bytes of each of 32 rows (8 stores instead of 16 of 16 bytes).
+    auto finish_item = [&](const Item& it) {
+      const int qi = it.qb * kBQ + wave * kQW + col;
+      const float l_tot = sum_halves(l_run);
+      const float inv = 1.0f / l_tot;  // rows past S (l = 0) are not stored
+      uint16_t* const orow = O + (size_t)it.bh * S * D + (size_t)min(qi, S - 1) * D;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db)
+  #pragma unroll
+        for (int rg = 0; rg < 4; rg += 2) {
+          const f32x4_t v0 = {oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv,
+                              oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv};
+          const f32x4_t v1 = {oacc[db][4 * rg + 4] * inv, oacc[db][4 * rg + 5] * inv,
+                              oacc[db][4 * rg + 6] * inv, oacc[db][4 * rg + 7] * inv};
+          // a0: columns 32db + 8rg + 4half + 0..3, a1: the same for rg + 1
+          const u32x2_t a0 = __builtin_bit_cast(u32x2_t, __builtin_convertvector(v0, bf16x4_t));
+          const u32x2_t a1 = __builtin_bit_cast(u32x2_t, __builtin_convertvector(v1, bf16x4_t));
+          // the lower half-wave keeps piece rg and needs its partner's a0; the
+          // upper keeps piece rg + 1 and needs its partner's a1
+          u32x2_t got;
+  #pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const unsigned send = half ? a0[e] : a1[e];
+            const auto p = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+            got[e] = half ? p[0] : p[1];
+          }
+          const u32x4_t piece = half ? (u32x4_t){got[0], got[1], a1[0], a1[1]} : (u32x4_t){a0[0], a0[1], got[0], got[1]};
+          if (qi < S) *reinterpret_cast<u32x4_t*>(orow + 32 * db + 8 * (rg + half)) = piece;
+        }
+      if (LSE && half == 0 && qi < S) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * common::kLn2;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
+      m_run = -__builtin_inff();
+      l_run = 0.f;
+    };
+
+    // ---- softmax phase for tile t of item `it` (flattened index T): S -> bf16
+    // P, running max / sum.  The NL load steps of copy cp are issued along the
+    // way, one per KS / NL exponential steps (pinned there by a scheduling
+    // barrier).  When `next_q` is set the next item's Q operand has already been
+    // loaded over this item's (its latency hidden by this phase), and the rare
+    // recompute below reloads this item's first.
+    auto softmax_phase = [&](const Item& it, int t, int T, const Copy& cp, bool next_q, const Item& nx) {
+      const int q0w = it.qb * kBQ + wave * kQW;
+      // tiles this wave takes part in (its rows see keys below min(S, q0w + 32))
+      const int n_w = q0w >= S ? 0 : (CAUSAL ? min(it.n_tiles, (min(q0w + kQW, S) - 1) / BK + 1) : it.n_tiles);
+      // the copy offsets are formed here, not hoisted out of the loop, where
+      // they would hold registers through the matrix phase
+      unsigned off0 = g_off;
+      asm volatile("" : "+v"(off0));
+      auto copy_at = [&](int ks) {
+        if (ks % (KS / NL) == 0) {
+          copy_step(ks / (KS / NL), cp, off0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (t >= n_w) {
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) set_p(ks, (bf16x8_t){});
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) copy_at(ks);
+        return;
+      }
+      const int kv0 = t * BK;
+      const int qi = q0w + col;
+      // Tiles that straddle the diagonal or run past S move to the base-2 domain
+      // here, so a hidden score is a plain -inf even when the scale is 0.
+      const bool masked = (CAUSAL && kv0 + BK - 1 > q0w) || kv0 + BK > S;
+      const float c_t = masked ? 1.f : c_log2;
+      auto apply_mask = [&]() {
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kj = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool hidden = (CAUSAL && kj > qi) || kj >= S;
+            sacc[kb][r] = hidden ? -__builtin_inff() : sacc[kb][r] * c_log2;
+          }
+      };
       if (masked) apply_mask();
-      take_exact_max();
-      exponentiate(F_{});
-    }
-    l_run += rs;
-  };
-
-  // ---- prologue: group 0 copies K_0 and K_1 and waits for K_0; group 1
-  // zero-fills the V slot that the first matrix phase reads with zero
-  // probabilities (V_0 is copied in phase 0)
-  if (grp == 0) {
-    const Copy k0 = next_copy(), k1 = next_copy();
-#pragma unroll
-    for (int i = 0; i < NL; ++i) copy_step(i, k0, g_off);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) copy_step(i, k1, g_off);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
-  } else {
-    char* v_prev = vbuf0 + vslot(-1) * G::kTileBytes;
-    for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
-      *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the zeros are in LDS
-  }
-  phase_barrier();
-
-  // ---- 2 (N + 1) phases, one barrier each.  The two groups run the same
-  // phases with their roles swapped.  Group 0 copies K_{T+2} during phase
-  // 2T+1 into the slot last read in phase 2T-1 and, before the barrier
-  // closing phase 2T+1, waits for K_{T+1} (its copy from phase 2T-1).  Group 1
-  // copies V_T during phase 2T into the slot last read in phase 2T-1 and waits
-  // for it before the barrier closing phase 2T+1.  So K_{T+1} and V_T are in
-  // LDS before their first reader, phase 2T+2.  In the softmax phase of an
-  // item's first tile the previous item is written out first; in that of its
-  // last tile the next item's Q operand is loaded first.
-  Item prev = cur;
-  int T = 0;
-  // the softmax phase of tile t of the current item (flattened index T)
-  auto softmax_step = [&](int t, const Item& nx) {
-    const Copy cp = next_copy();
-    if (t == 0 && T > 0) finish_item(prev);
-    const bool next_q = t + 1 == cur.n_tiles && nx.valid;
-    if (next_q) load_q(nx);
-    softmax_phase(cur, t, T, cp, next_q, nx);
-  };
-  if (grp == 0) {
-    matrix_phase(0);  // phase 0
-    phase_barrier();
-    for (;;) {
-      const Item nx = item_at(cur.k + 1);
-      for (int t = 0; t < cur.n_tiles; ++t, ++T) {
-        softmax_step(t, nx);  // phase 2T + 1
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
-        phase_barrier();
-        matrix_phase(T + 1);  // phase 2T + 2
-        phase_barrier();
+      // exponentiate against the running maximum (the copies interleaved when
+      // COPIES); rs is the lane's share of the tile's row sum
+      float rs = 0.f;
+      auto exponentiate = [&](auto copies_c) {
+        constexpr bool COPIES = decltype(copies_c)::value;
+        const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
+        rs = 0.f;
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int kb = ks >> 1, r0 = 8 * (ks & 1);
+          bf16x8_t p8;
+  #pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const f32x2_t x = {__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e], c_t, neg_m)),
+                               __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e + 1], c_t, neg_m))};
+            rs += x[0];
+            rs += x[1];
+            const bf16x2_t b = __builtin_convertvector(x, bf16x2_t);
+            p8[e] = b[0];
+            p8[e + 1] = b[1];
+          }
+          set_p(ks, p8);
+          if constexpr (COPIES) copy_at(ks);
+        }
+      };
+      // The first tile sets the running maximum exactly.  Later tiles
+      // exponentiate against it at once; only if some row's tile sum then passes
+      // 2^64 (a score about 58 above the running maximum, base 2) is the tile
+      // redone: its scores, which the probabilities have overwritten, are
+      // recomputed from K_T (still in its LDS slot: K_{T+3} is copied two phases
+      // later), the maximum is taken exactly, and O and l are rescaled.
+      // (the maximum of the scaled scores: the scale may be negative)
+      auto take_exact_max = [&]() {
+        float mxk[KB];  // one three-input max chain per 32-key block
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          mxk[kb] = fmaxf(sacc[kb][0] * c_t, sacc[kb][1] * c_t);
+  #pragma unroll
+          for (int r = 2; r < 16; r += 2) mxk[kb] = max3(mxk[kb], sacc[kb][r] * c_t, sacc[kb][r + 1] * c_t);
+        }
+        float mx = mxk[0];
+  #pragma unroll
+        for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mxk[kb]);
+        const float m_new = fmaxf(m_run, max_halves(mx));
+        const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      };
+      if (t == 0) take_exact_max();
+      exponentiate(T_{});
+      if (t > 0 && __builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
+        if (next_q) load_q(it);
+        const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(T) * G::kTileBytes);
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+          for (int ds = 0; ds < DS; ++ds) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);  // one operand read at a time: this path is rare
+          }
+        if (next_q) load_q(nx);
+        if (masked) apply_mask();
+        take_exact_max();
+        exponentiate(F_{});
       }
-      prev = cur;
-      if (!nx.valid) break;
-      cur = nx;
+      l_run += rs;
+    };
+
+    // ---- prologue: group 0 copies K_0 and K_1 and waits for K_0; group 1
+    // zero-fills the V slot that the first matrix phase reads with zero
+    // probabilities (V_0 is copied in phase 0)
+    if (grp == 0) {
+      const Copy k0 = next_copy(), k1 = next_copy();
+  #pragma unroll
+      for (int i = 0; i < NL; ++i) copy_step(i, k0, g_off);
+  #pragma unroll
+      for (int i = 0; i < NL; ++i) copy_step(i, k1, g_off);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
+    } else {
+      char* v_prev = vbuf0 + vslot(-1) * G::kTileBytes;
+      for (int off = gtid * 16; off < G::kTileBytes; off += kGroupThreads * 16)
+        *reinterpret_cast<u32x4_t*>(v_prev + off) = (u32x4_t){0u, 0u, 0u, 0u};
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the zeros are in LDS
     }
-    finish_item(prev);  // phase 2N + 1
     phase_barrier();
-  } else {
-    {  // phase 0: no scores yet, only the copy of V_0
+
+    // ---- 2 (N + 1) phases, one barrier each.  The two groups run the same
+    // phases with their roles swapped.  Group 0 copies K_{T+2} during phase
+    // 2T+1 into the slot last read in phase 2T-1 and, before the barrier
+    // closing phase 2T+1, waits for K_{T+1} (its copy from phase 2T-1).  Group 1
+    // copies V_T during phase 2T into the slot last read in phase 2T-1 and waits
+    // for it before the barrier closing phase 2T+1.  So K_{T+1} and V_T are in
+    // LDS before their first reader, phase 2T+2.  In the softmax phase of an
+    // item's first tile the previous item is written out first; in that of its
+    // last tile the next item's Q operand is loaded first.
+    Item prev = cur;
+    int T = 0;
+    // the softmax phase of tile t of the current item (flattened index T)
+    auto softmax_step = [&](int t, const Item& nx) {
       const Copy cp = next_copy();
-#pragma unroll
-      for (int i = 0; i < NL; ++i) copy_step(i, cp, g_off);
-    }
-    phase_barrier();
-    matrix_phase(0);  // phase 1
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
-    phase_barrier();
-    for (;;) {
-      const Item nx = item_at(cur.k + 1);
-      for (int t = 0; t < cur.n_tiles; ++t, ++T) {
-        softmax_step(t, nx);  // phase 2T + 2
-        phase_barrier();
-        matrix_phase(T + 1);  // phase 2T + 3
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
-        phase_barrier();
+      if (t == 0 && T > 0) finish_item(prev);
+      const bool next_q = t + 1 == cur.n_tiles && nx.valid;
+      if (next_q) load_q(nx);
+      softmax_phase(cur, t, T, cp, next_q, nx);
+    };
+    if (grp == 0) {
+      matrix_phase(0);  // phase 0
+      phase_barrier();
+      for (;;) {
+        const Item nx = item_at(cur.k + 1);
+        for (int t = 0; t < cur.n_tiles; ++t, ++T) {
+          softmax_step(t, nx);  // phase 2T + 1
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
+          phase_barrier();
+          matrix_phase(T + 1);  // phase 2T + 2
+          phase_barrier();
+        }
+        prev = cur;
+        if (!nx.valid) break;
+        cur = nx;
       }
-      prev = cur;
-      if (!nx.valid) break;
-      cur = nx;
+      finish_item(prev);  // phase 2N + 1
+      phase_barrier();
+    } else {
+      {  // phase 0: no scores yet, only the copy of V_0
+        const Copy cp = next_copy();
+  #pragma unroll
+        for (int i = 0; i < NL; ++i) copy_step(i, cp, g_off);
+      }
+      phase_barrier();
+      matrix_phase(0);  // phase 1
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+      phase_barrier();
+      for (;;) {
+        const Item nx = item_at(cur.k + 1);
+        for (int t = 0; t < cur.n_tiles; ++t, ++T) {
+          softmax_step(t, nx);  // phase 2T + 2
+          phase_barrier();
+          matrix_phase(T + 1);  // phase 2T + 3
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+          phase_barrier();
+        }
+        prev = cur;
+        if (!nx.valid) break;
+        cur = nx;
+      }
+      finish_item(prev);
     }
-    finish_item(prev);
+    // no global->LDS copy may still be writing when the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+  };
+  const Item first = static_item(0);
+  if (first.valid) run_segment(first, F_{});
+  if constexpr (BALANCED) {
+    for (;;) {
+      const Item it = claim();
+      if (!it.valid) break;
+      run_segment(it, T_{});
+    }
+    // This workgroup has made its last claim, and once every wave has read it
+    // the slot is cleared.  The last workgroup to get here (all claims are
+    // over) zeroes the counters: the workspace is left as it was found.
+    phase_barrier();
+    if (wave == 0 && lane_id() == 0) {
+      unsigned* const slot = sched + kSchedSlots + 2 * blockIdx.x;
+      __hip_atomic_store(slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned done = __hip_atomic_fetch_add(&sched[kSchedDone], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == gridDim.x - 1) {
+        for (int y = 0; y < 8; ++y) __hip_atomic_store(&sched[32 * y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&sched[kSchedDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
-  // no global->LDS copy may still be writing when the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
 }
 
 }  // namespace pp
