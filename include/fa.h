@@ -110,7 +110,7 @@ fa_status fa_fwd_variant(const void *q, const void *k, const void *v, void *o, f
  * clock, so a static split ends with the slowest XCD.  In every other case
  * the call runs exactly as fa_fwd and the workspace is not touched.
  *
- *   workspace  device memory owned by the caller, 4-byte aligned, at least
+ *   workspace  device memory owned by the caller, 8-byte aligned, at least
  *              fa_fwd_workspace_bytes() bytes, ZERO-FILLED before its first
  *              use (e.g. one hipMemset).  Every call leaves it zero-filled
  *              again: its last workgroup resets the counters.  A workspace

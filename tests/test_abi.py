@@ -188,7 +188,7 @@ def test_fwd_ws_rejects_before_launch():
     """fa_fwd_ws checks its workspace, then everything fa_fwd checks; nothing is launched."""
     assert _fwd_ws(ws=0) == fa.FA_ERR_INVALID_ARGUMENT               # no workspace
     assert _fwd_ws(ws_bytes=8191) == fa.FA_ERR_INVALID_ARGUMENT      # too small
-    assert _fwd_ws(ws=P + 2) == fa.FA_ERR_INVALID_ARGUMENT           # misaligned
+    assert _fwd_ws(ws=P + 4) == fa.FA_ERR_INVALID_ARGUMENT           # not 8-byte aligned
     assert _fwd_ws(ptrs=(P, P, 0, P)) == fa.FA_ERR_INVALID_ARGUMENT
     assert _fwd_ws(B=0) == fa.FA_ERR_INVALID_ARGUMENT
     assert _fwd_ws(scale=float("inf")) == fa.FA_ERR_INVALID_ARGUMENT

@@ -300,7 +300,7 @@ int64_t fa_fwd_workspace_bytes(void) { return fa::pp::kSchedBytes; }
 fa_status fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                     int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, void* workspace,
                     int64_t workspace_bytes, void* stream) {
-  if (!workspace || !aligned(workspace, 4) || workspace_bytes < fa::pp::kSchedBytes) return FA_ERR_INVALID_ARGUMENT;
+  if (!workspace || !aligned(workspace, 8) || workspace_bytes < fa::pp::kSchedBytes) return FA_ERR_INVALID_ARGUMENT;
   return fwd_impl(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, FA_VARIANT_AUTO,
                   static_cast<unsigned*>(workspace), stream);
 }

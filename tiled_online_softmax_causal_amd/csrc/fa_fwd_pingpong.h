@@ -86,8 +86,9 @@ constexpr int kBQ = kQW * kWaves;       // query rows per workgroup
 constexpr int kAhead = 5;               // MFMAs between an operand's LDS read and its use
 constexpr float kOverflowSum = 0x1p64f; // a tile sum above this redoes the tile with the exact maximum
 // Balanced schedule's workspace (32-bit words): 8 pool counters 128 bytes apart
-// (words 0, 32, ..., 224), a count of finished workgroups (word 256), then one
-// 8-byte broadcast slot per workgroup from word 288.  It is zero between calls.
+// (64-bit front/back pairs at words 0, 32, ..., 224), a count of finished
+// workgroups (word 256), then one 8-byte broadcast slot per workgroup from
+// word 288.  It is zero between calls.
 constexpr int kSchedBytes = 8192;
 constexpr int kSchedDone = 256;
 constexpr int kSchedSlots = 288;
@@ -185,16 +186,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   // and a static schedule ends with the slowest XCD.  So the last eighth of
   // every XCD's heads (hp of its hx heads) form a pool instead of being
   // scheduled in advance.  A workgroup that has finished its static items
-  // claims pool items one at a time with an atomic counter per XCD: first its
-  // own XCD's pool, then the other XCDs'.  A pool hands out its items heaviest
-  // first across its heads (every head's last query block, then the one
-  // before, ...), so that the last claims are the shortest items.  Each
-  // claimed item runs as a pipeline of its own.  Which workgroup computes an
-  // item does not change its arithmetic, so the outputs equal the static
-  // schedule's bit for bit.
-  // sched: 8 counters 128 bytes apart, a done count, then one (bh, qb) slot per
-  // workgroup.  The counters start at zero, and the last workgroup to finish
-  // zeroes them again for the next call.
+  // claims pool items one at a time.  It takes its own XCD's pool from the
+  // front, head after head, heaviest query block first, so that the XCD's
+  // workgroups share each head's K/V in their L2.  Once that pool is empty it
+  // takes other XCDs' pools from the back, where their lightest items are,
+  // which read the least K/V from outside its L2.  Front and back counts of a
+  // pool share one 64-bit word, so one atomic add claims an item and never
+  // one that the other end has taken.  Each claimed item runs as a pipeline
+  // of its own.  Which workgroup computes an item does not change its
+  // arithmetic, so the outputs equal the static schedule's bit for bit.
+  // sched: 8 front/back counters 128 bytes apart, a done count, then one
+  // (bh, qb) slot per workgroup.  The counters start at zero, and the last
+  // workgroup to finish zeroes them again for the next call.
   const int hx = n_items / (8 * n_qb);           // heads per XCD
   const int hp = BALANCED ? max(1, hx / 8) : 0;  // of them in the pool
   const int pool_base = (hx - hp) * n_qb;        // the XCD's static items come before it
@@ -227,12 +230,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     if (wave == 0 && lane_id() == 0) {
       const int x = blockIdx.x & 7;
       int b = -1, q = 0;
+      const int len = hp * n_qb;  // pool position i: head i / n_qb of the pool, block n_qb - 1 - i % n_qb
       for (int d = 0; d < 8 && b < 0; ++d) {
         const int y = (x + d) & 7;
-        const unsigned i = __hip_atomic_fetch_add(&sched[32 * y], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (i < (unsigned)(hp * n_qb)) {  // pool position i: weight rank i / hp of pool head i % hp
-          b = (hx - hp + (int)i % hp) * 8 + y;
-          q = n_qb - 1 - (int)i / hp;
+        const unsigned long long old = __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(&sched[32 * y]),
+                                                              d == 0 ? 1ull : 1ull << 32, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT);
+        const int front = (int)(unsigned)old, back = (int)(unsigned)(old >> 32);
+        if (front + back < len) {
+          const int i = d == 0 ? front : len - 1 - back;
+          b = (hx - hp + i / n_qb) * 8 + y;
+          q = n_qb - 1 - i % n_qb;
         }
       }
       __hip_atomic_store(slot, (unsigned)b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -668,7 +676,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       __hip_atomic_store(slot + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const unsigned done = __hip_atomic_fetch_add(&sched[kSchedDone], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
       if (done == gridDim.x - 1) {
-        for (int y = 0; y < 8; ++y) __hip_atomic_store(&sched[32 * y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int y = 0; y < 8; ++y)
+          __hip_atomic_store(reinterpret_cast<unsigned long long*>(&sched[32 * y]), 0ull, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&sched[kSchedDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
