@@ -284,13 +284,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     auto load_q = [&](const Item& it) {
       const int qrow = min(it.qb * kBQ + wave * kQW + col, S - 1);
       const uint16_t* src = Q + (size_t)it.bh * S * D + (size_t)qrow * D + 8 * half;
-  #pragma unroll
+#pragma unroll
       for (int ds = 0; ds < DS; ++ds) qreg[ds] = *reinterpret_cast<const bf16x8_t*>(src + 16 * ds);
     };
     load_q(cur);
 
     f32x16_t oacc[DB];
-  #pragma unroll
+#pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
     // Scores and probabilities share registers: the bf16 probabilities of
     // k-step ks (keys 16*ks.., 8 per lane) are written over the first four of
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     // read from there as the B operand of the P.V MFMA before the next score
     // MFMAs overwrite the accumulator.
     f32x16_t sacc[KB];
-  #pragma unroll
+#pragma unroll
     for (int kb = 0; kb < KB; ++kb) sacc[kb] = (f32x16_t){};
     auto p_operand = [&](int ks) {
       const f32x16_t& a = sacc[ks >> 1];
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     auto set_p = [&](int ks, bf16x8_t p8) {
       const f32x4_t w = __builtin_bit_cast(f32x4_t, p8);
       const int r0 = 8 * (ks & 1);
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < 4; ++j) sacc[ks >> 1][r0 + j] = w[j];
     };
     float m_run = -__builtin_inff(), l_run = 0.f;
@@ -370,12 +370,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     int k_off[DS], v_off_lo[DB], v_off_hi[DB];
     {
       const int sk = swz<G::kChunks>(col);
-  #pragma unroll
+#pragma unroll
       for (int ds = 0; ds < DS; ++ds) k_off[ds] = col * G::kRowBytes + (((2 * ds + half) ^ sk) << 4);
       const int vr = 4 * half + (u >> 2);
       const int s_lo = swz<G::kChunks>(vr), s_hi = swz<G::kChunks>(vr + 8);
       const int c_l = 2 * (quad & 1) + ((u & 3) >> 1);
-  #pragma unroll
+#pragma unroll
       for (int db = 0; db < DB; ++db) {
         v_off_lo[db] = vr * G::kRowBytes + (((4 * db + c_l) ^ s_lo) << 4) + 8 * (u & 1);
         v_off_hi[db] = (vr + 8) * G::kRowBytes + (((4 * db + c_l) ^ s_hi) << 4) + 8 * (u & 1);
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       // the matrix-core wave issues first; the softmax wave on the same SIMD
       // fills the issue slots the MFMAs leave free
       __builtin_amdgcn_s_setprio(1);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < NM; ++i) {
         if (i < NPV) {
           const int ks = i / DB, db = i % DB;
@@ -430,9 +430,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       const float l_tot = sum_halves(l_run);
       const float inv = 1.0f / l_tot;  // rows past S (l = 0) are not stored
       uint16_t* const orow = O + (size_t)it.bh * S * D + (size_t)min(qi, S - 1) * D;
-  #pragma unroll
+#pragma unroll
       for (int db = 0; db < DB; ++db)
-  #pragma unroll
+#pragma unroll
         for (int rg = 0; rg < 4; rg += 2) {
           const f32x4_t v0 = {oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv,
                               oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv};
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           // the lower half-wave keeps piece rg and needs its partner's a0; the
           // upper keeps piece rg + 1 and needs its partner's a1
           u32x2_t got;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 2; ++e) {
             const unsigned send = half ? a0[e] : a1[e];
             const auto p = __builtin_amdgcn_permlane32_swap(send, send, false, false);
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           if (qi < S) *reinterpret_cast<u32x4_t*>(orow + 32 * db + 8 * (rg + half)) = piece;
         }
       if (LSE && half == 0 && qi < S) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * common::kLn2;
-  #pragma unroll
+#pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
       m_run = -__builtin_inff();
       l_run = 0.f;
@@ -481,9 +481,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
         }
       };
       if (t >= n_w) {
-  #pragma unroll
+#pragma unroll
         for (int ks = 0; ks < KS; ++ks) set_p(ks, (bf16x8_t){});
-  #pragma unroll
+#pragma unroll
         for (int ks = 0; ks < KS; ++ks) copy_at(ks);
         return;
       }
@@ -494,9 +494,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       const bool masked = (CAUSAL && kv0 + BK - 1 > q0w) || kv0 + BK > S;
       const float c_t = masked ? 1.f : c_log2;
       auto apply_mask = [&]() {
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
             const bool hidden = (CAUSAL && kj > qi) || kj >= S;
@@ -511,11 +511,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
         constexpr bool COPIES = decltype(copies_c)::value;
         const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
         rs = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int kb = ks >> 1, r0 = 8 * (ks & 1);
           bf16x8_t p8;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; e += 2) {
             const f32x2_t x = {__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e], c_t, neg_m)),
                                __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e + 1], c_t, neg_m))};
@@ -538,19 +538,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       // (the maximum of the scaled scores: the scale may be negative)
       auto take_exact_max = [&]() {
         float mxk[KB];  // one three-input max chain per 32-key block
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           mxk[kb] = fmaxf(sacc[kb][0] * c_t, sacc[kb][1] * c_t);
-  #pragma unroll
+#pragma unroll
           for (int r = 2; r < 16; r += 2) mxk[kb] = max3(mxk[kb], sacc[kb][r] * c_t, sacc[kb][r + 1] * c_t);
         }
         float mx = mxk[0];
-  #pragma unroll
+#pragma unroll
         for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mxk[kb]);
         const float m_new = fmaxf(m_run, max_halves(mx));
         const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
-  #pragma unroll
+#pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         m_run = m_new;
       };
@@ -559,9 +559,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       if (t > 0 && __builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
         if (next_q) load_q(it);
         const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(T) * G::kTileBytes);
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int ds = 0; ds < DS; ++ds) {
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Kl + 32 * kb * G::kRowBytes + k_off[ds]);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], ds == 0 ? (f32x16_t){} : sacc[kb], 0, 0, 0);
@@ -580,9 +580,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     // probabilities (V_0 is copied in phase 0)
     if (grp == 0) {
       const Copy k0 = next_copy(), k1 = next_copy();
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < NL; ++i) copy_step(i, k0, g_off);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < NL; ++i) copy_step(i, k1, g_off);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
     } else {
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     } else {
       {  // phase 0: no scores yet, only the copy of V_0
         const Copy cp = next_copy();
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < NL; ++i) copy_step(i, cp, g_off);
       }
       phase_barrier();
