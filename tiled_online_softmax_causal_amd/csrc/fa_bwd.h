@@ -34,6 +34,8 @@
 // in the matching row order.
 #pragma once
 
+#include <utility>
+
 #include "fa_common.h"
 #include "fa_mfma_bf16.h"
 
@@ -44,6 +46,23 @@ constexpr int kRows = 32 * kWaves;  // query rows (dQ kernel) or keys (dK/dV ker
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// Issue order of a run of N steps of M MFMAs, each step taking R LDS reads for
+// its A operands: first PRE other reads (row values the run's elementwise work
+// needs) and the reads of the first A steps, then each step's MFMAs followed by
+// the reads of step i + A.  Left to itself the compiler reads each operand
+// right before its MFMA and waits for it there, so every MFMA pays the LDS
+// latency; A steps of lead hide it.
+template <int N, int M, int R, int A, int PRE, int... I>
+__device__ __forceinline__ void pipeline_reads(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE + R * (N < A ? N : A), 0);  // DS reads
+  ((__builtin_amdgcn_sched_group_barrier(0x008, M, 0),                         // MFMAs of step I
+    (I + A < N ? __builtin_amdgcn_sched_group_barrier(0x100, R, 0) : void())), ...);
+}
+template <int N, int M, int R, int A, int PRE = 0>
+__device__ __forceinline__ void pipeline_reads() {
+  pipeline_reads<N, M, R, A, PRE>(std::make_integer_sequence<int, N>{});
+}
 
 // Copy ROWS rows of X starting at r0 (rows past S re-read row S-1) into a
 // swizzled LDS tile, HBM -> LDS directly (global_load_lds, no register
@@ -189,6 +208,8 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dq(
           pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_rows<D>(Vl, kb, ds, col, half), doreg[ds], pacc[kb], 0, 0, 0);
         }
       }
+      pipeline_reads<KB * DS, 2, 2, 2>();
+      __builtin_amdgcn_sched_barrier(0);
       // dS = P * (dP - delta); hidden keys (above the diagonal or past S) give 0
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -207,6 +228,7 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dq(
         for (int db = 0; db < DB; ++db)
           qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_transposed<D>(Kl, db, ks, lane), dsb, qacc[db], 0, 0, 0);
       }
+      pipeline_reads<KS * DB, 1, 2, 4>();
     }
     __builtin_amdgcn_s_waitcnt(common::waitcnt_vm<0>());  // the next tile has landed
     __syncthreads();
@@ -305,6 +327,8 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dkdv(
           pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_rows<D>(dOl, qb, ds, col, half), vreg[ds], pacc[qb], 0, 0, 0);
         }
       }
+      pipeline_reads<QB * DS, 2, 3, 1>();
+      __builtin_amdgcn_sched_barrier(0);
       // P and dS = P * (dP - delta); hidden pairs (key above the query, or a
       // query row past S) give 0
 #pragma unroll
@@ -323,6 +347,7 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dkdv(
             xacc[qb][r] = p;
           }
         }
+      __builtin_amdgcn_sched_barrier(0);
       // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -334,6 +359,7 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_bwd_dkdv(
           dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_transposed<D>(Ql, db, ks, lane), dsb, dkacc[db], 0, 0, 0);
         }
       }
+      pipeline_reads<KS * DB, 2, 4, 1>();
     }
     if (has_next && tid < 2 * QT) rows[st ^ 1][tid / QT][tid % QT] = rv;
     __builtin_amdgcn_s_waitcnt(common::waitcnt_vm<0>());  // the next tiles have landed
