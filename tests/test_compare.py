@@ -6,7 +6,7 @@ gfx950), and one call of each path with known counter values.
 """
 import csv
 
-from tiled_online_softmax_causal_amd.compare import clock, traffic
+from tiled_online_softmax_causal_amd.compare import clock, page_grid, traffic, traffic_by_call
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 
@@ -62,3 +62,35 @@ def test_clock_from_busy_cycles(tmp_path):
                         "Counter_Value": value, "Start_Timestamp": 1000, "End_Timestamp": 1000 + ns})
     out = clock(str(tmp_path / "g.csv"))
     assert out == {"bwd": {"ghz": 2.0, "dispatches": 1}, "flash": {"ghz": 1.8, "dispatches": 2}}
+
+
+def test_traffic_split_per_call(tmp_path):
+    """Two lengths, one call per path each: a tiled dispatch opens each call; the dense
+    dispatches (3 kernels; 2 head chunks at the second length) after it belong to it."""
+    kib = 1024 * 1024
+    _write(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", kib / 2)])
+    _write(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", kib)])
+    gen = ("distribution_elementwise_grid_stride_kernel", 5.0)
+    fl = "void fa::pp::attn_fwd_pingpong<128, 128, true, true>(...)"
+    small = "void fa::mfma::attn_fwd_mfma_bf16<128, 64, 64, true>(...)"
+    dn = ["void fa::dense::dense_scores<128, true>(...)", "void fa::dense::dense_softmax<true>(...)",
+          "void fa::dense::dense_pv<128, true>(...)"]
+    seq = [gen, (small, 1.0)] + [(k, 2.0) for k in dn] + [gen, (fl, 10.0)] + [(k, 3.0) for k in dn + dn]
+    _write(tmp_path / "f.csv", [(n, "FETCH_SIZE", v) for n, v in seq])
+    _write(tmp_path / "w.csv", [(n, "WRITE_SIZE", v / 2) for n, v in seq])
+    calls = traffic_by_call(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                            str(tmp_path / "cw.csv"))
+    assert len(calls) == 2
+    assert calls[0]["flash"] == {"read_bytes": 2048, "write_bytes": 512, "dispatches": 1, "total_bytes": 2560}
+    assert calls[0]["dense"] == {"read_bytes": 3 * 4096, "write_bytes": 3 * 1024, "dispatches": 3,
+                                 "total_bytes": 15 * 1024}
+    assert calls[1]["flash"]["read_bytes"] == 20 * 1024 and calls[1]["flash"]["write_bytes"] == 5 * 1024
+    assert calls[1]["dense"]["dispatches"] == 6 and calls[1]["dense"]["read_bytes"] == 6 * 6 * 1024
+
+
+def test_page_grid():
+    """The model's profile grid: 48 lengths from 512 to 131072, each step x 256^(1/47)."""
+    g = page_grid()
+    assert len(g) == 48 and g[0] == 512 and g[-1] == 131072
+    assert g[1] == 576 and g[2] == 648  # 512 * 1.12522 = 576.1, * 1.12522^2 = 648.3
+    assert all(b > a for a, b in zip(g, g[1:]))

@@ -85,6 +85,48 @@ def traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv:
     return out
 
 
+def _dispatch_kib(path: str) -> list:
+    """(dispatch id, path, KiB) of each counted dispatch, in dispatch order."""
+    with open(path) as f:
+        rows = [(int(r["Dispatch_Id"]), _path_of(r["Kernel_Name"]), float(r["Counter_Value"])) for r in csv.DictReader(f)]
+    return sorted(r for r in rows if r[1] is not None)
+
+
+def traffic_by_call(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                    copy_mib: int = 1024) -> list:
+    """HBM bytes of each call, in call order, for a run of one call per path at each
+    sequence length (compare.py --steps 1 --warmup 0): every tiled dispatch opens a call,
+    and the dense dispatches after it (one per kernel and head chunk) belong to it."""
+    f_fac = copy_mib * 1024 / _copy_kib(copy_fetch_csv)
+    w_fac = copy_mib * 1024 / _copy_kib(copy_write_csv)
+    calls = []
+    for rows, key, fac in ((_dispatch_kib(fetch_csv), "read_bytes", f_fac), (_dispatch_kib(write_csv), "write_bytes", w_fac)):
+        i = -1
+        for _, p, kib in rows:
+            if p == "flash":
+                i += 1
+            if i < 0:
+                raise SystemExit(f"a {p} dispatch before the first tiled one")
+            if i == len(calls):
+                calls.append({})
+            d = calls[i].setdefault(p, {"read_bytes": 0.0, "write_bytes": 0.0, "dispatches": 0})
+            d[key] += kib * 1024 * fac
+            if key == "read_bytes":
+                d["dispatches"] += 1
+    for c in calls:
+        for d in c.values():
+            d["read_bytes"], d["write_bytes"] = int(d["read_bytes"]), int(d["write_bytes"])
+            d["total_bytes"] = d["read_bytes"] + d["write_bytes"]
+    return calls
+
+
+def page_grid() -> list:
+    """The 48 sequence lengths of the reduced-order model's profile curves, rounded."""
+    from tiled_online_softmax_causal_amd.costmodel import page_profile_seqs
+
+    return [int(round(s)) for s in page_profile_seqs()]
+
+
 def clock(grbm_csv: str, n_xcd: int = 8) -> dict:
     """Mean GPU clock (GHz) over each path's dispatches: GRBM_GUI_ACTIVE, the cycles the
     graphics engine is busy, summed over the n_xcd XCDs, divided by the dispatch's duration."""
@@ -105,7 +147,8 @@ def clock(grbm_csv: str, n_xcd: int = 8) -> dict:
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--seq", default="1024,4096,16384,32768")
+    ap.add_argument("--seq", default="1024,4096,16384,32768",
+                    help="comma list of sequence lengths, or 'grid48': the model's 48-point profile grid")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--dim", type=int, default=128)
@@ -117,6 +160,8 @@ def main():
                     help="workspace of the dense path; heads are processed in chunks that fit")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
     ap.add_argument("--calls", type=int, default=1, help="attention calls per path in the profiled run")
+    ap.add_argument("--per-call", action="store_true",
+                    help="with --traffic: one line per call (one call per path at each --seq length)")
     ap.add_argument("--inputs", choices=("uniform", "zeros"), default="uniform",
                     help="uniform(-0.8, 0.8) (the workload) or all-zero Q, K, V: the same instructions with "
                          "no switching in the matrix-core operands, to separate power from issue limits")
@@ -125,6 +170,14 @@ def main():
     args = ap.parse_args()
     if args.clock:
         print(json.dumps(clock(args.clock)))
+        return
+    seqs = page_grid() if args.seq == "grid48" else [int(s) for s in args.seq.split(",")]
+    if args.traffic and args.per_call:
+        calls = traffic_by_call(*args.traffic)
+        if len(calls) != len(seqs):
+            raise SystemExit(f"{len(calls)} calls in the counter files, {len(seqs)} lengths in --seq")
+        for S, c in zip(seqs, calls):
+            print(json.dumps({"seq_len": S, **c}))
         return
     if args.traffic:
         print(json.dumps(traffic(*args.traffic, calls=args.calls)))
@@ -145,7 +198,7 @@ def main():
     for v in args.variants.split(","):
         if v not in fa.VARIANTS:
             raise SystemExit(f"unknown variant {v}; one of {sorted(fa.VARIANTS)}")
-    for S in (int(s) for s in args.seq.split(",")):
+    for S in seqs:
         q, k, v = uniform_qkv_device(B, H, S, D, seed=42, dtype=torch.bfloat16, device=dev)
         if args.inputs == "zeros":
             for t in (q, k, v):
