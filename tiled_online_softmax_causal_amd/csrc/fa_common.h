@@ -80,7 +80,13 @@ __device__ __forceinline__ void schedule_block(int wg, int n_qb, int xcd_group, 
 // of an XCD take the XCD's items P at a time in the heaviest-first order, the
 // order reversed every other round ("snake"), so that over two rounds every
 // workgroup gets about the same work and the workgroups of an XCD stay on
-// the same or adjacent heads, sharing their K/V in that XCD's L2.
+// the same or adjacent heads, sharing their K/V in that XCD's L2.  That
+// head-major order balances only when a head's n_qb items fill whole rounds
+// (n_qb a multiple of P); otherwise rounds straddle heads, and a workgroup can
+// draw the heaviest block of two heads twice (twice the mean work at
+// S = 7723, b1 h32).  With fewer than P heads per XCD the order is then
+// block-major instead: the XCD's heads take each query-block level in turn,
+// so every round holds items of near-equal weight.
 __device__ __forceinline__ bool next_item(int w, int k, int G, int n_qb, int n_items, int xcd_group, int& bh,
                                           int& qb) {
   if (G >= n_items) {
@@ -91,9 +97,14 @@ __device__ __forceinline__ bool next_item(int w, int k, int G, int n_qb, int n_i
   if (xcd_group && (G & 7) == 0) {
     const int P = G >> 3, xcd = w & 7, j = w >> 3;
     const int idx = P * k + ((k & 1) ? P - 1 - j : j);
-    if (idx >= (n_items >> 3)) return false;
-    bh = (idx / n_qb) * 8 + xcd;
-    qb = n_qb - 1 - idx % n_qb;
+    const int per_xcd = n_items >> 3;
+    if (idx >= per_xcd) return false;
+    const int hx = per_xcd / n_qb;  // heads per XCD
+    const bool block_major = n_qb % P != 0 && hx < P;
+    const int div = block_major ? hx : n_qb, a = idx / div, r = idx - a * div;
+    // wave-uniform; kept in SGPRs (the division is expanded on the vector unit)
+    bh = __builtin_amdgcn_readfirstlane((block_major ? r : a) * 8 + xcd);
+    qb = __builtin_amdgcn_readfirstlane(n_qb - 1 - (block_major ? a : r));
     return true;
   }
   const int item = w + G * k;
