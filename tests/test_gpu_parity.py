@@ -226,12 +226,14 @@ def test_long_sequences_sampled(B, H, S, n_rows):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("B,H,S", [(1, 5, 16384), (2, 8, 5000)])
+@pytest.mark.parametrize("B,H,S", [(1, 5, 16384), (2, 8, 5000), (1, 32, 7723), (1, 32, 2373)])
 def test_resident_grid_sequences(B, H, S):
     """More work items than CUs, so one resident workgroup per CU walks a sequence of
-    items: h5 (heads not grouped per XCD, items taken in strides of the grid) and
+    items: h5 (heads not grouped per XCD, items taken in strides of the grid),
     b2 h8 S5000 (grouped per XCD, 40 items per XCD for 32 workgroups: a partial
-    second round).  Sampled rows of every head."""
+    second round), and b1 h32 at S = 7723 and 2373 (31 and 10 query blocks per head,
+    not a multiple of the 32 workgroups of an XCD: the XCD's 4 heads are dealt block
+    by block).  Sampled rows of every head."""
     case(f"bf16 {B}x{H}x{S}x128 causal, resident grid")
     q, k, v = device_inputs(B, H, S, 128, seed=S)
     o, lse = run_fwd(q, k, v)
