@@ -233,11 +233,14 @@ def main():
     balanced = (use_ws and variant in (fa.FA_VARIANT_MFMA_B256, fa.FA_VARIANT_MFMA_B256_K128)
                 and (B * H) % 8 == 0 and B * H >= 64 and cus % 8 == 0 and n_items > cus)
 
+    # fa_fwd for the automatic variant, fa_fwd_variant for an explicit one
+    call_variant = "auto" if args.variant == "auto" else variant
+
     def step():
         if use_ws:
             fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse, stream=stream, workspace=ws)
         else:
-            fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse, variant=variant, stream=stream)
+            fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse, variant=call_variant, stream=stream)
 
     for _ in range(args.warmup):
         step()

@@ -226,17 +226,32 @@ def test_long_sequences_sampled(B, H, S, n_rows):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("B,H,S", [(1, 5, 16384), (2, 8, 5000), (1, 32, 7723), (1, 32, 2373)])
+def _run_poisoned(q, k, v, causal, scale):
+    """The forward into NaN-filled outputs; every element must come out finite (no
+    work item skipped, none written twice with a stale value)."""
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), "rows left unwritten"
+    return o, lse
+
+
+@pytest.mark.parametrize("B,H,S", [(1, 5, 16384), (2, 8, 5000), (1, 32, 7723), (1, 32, 2373), (1, 12, 8192),
+                                   (1, 20, 4096), (2, 32, 7723)])
 def test_resident_grid_sequences(B, H, S):
     """More work items than CUs, so one resident workgroup per CU walks a sequence of
     items: h5 (heads not grouped per XCD, items taken in strides of the grid),
     b2 h8 S5000 (grouped per XCD, 40 items per XCD for 32 workgroups: a partial
-    second round), and b1 h32 at S = 7723 and 2373 (31 and 10 query blocks per head,
-    not a multiple of the 32 workgroups of an XCD: the XCD's 4 heads are dealt block
-    by block).  Sampled rows of every head."""
+    second round), b1 h32 at S = 7723 and 2373 (31 and 10 query blocks per head,
+    not a multiple of the 32 workgroups of an XCD, where the cost model may deal an
+    XCD's heads block by block), b1 h12 and h20 (flat lists, heads not a multiple of
+    8) and b2 h32 S7723.  Items of odd rounds walk their keys from the diagonal
+    down.  Outputs start as NaN and must all come out finite; sampled rows of every
+    head against the oracle."""
     case(f"bf16 {B}x{H}x{S}x128 causal, resident grid")
     q, k, v = device_inputs(B, H, S, 128, seed=S)
-    o, lse = run_fwd(q, k, v)
+    o, lse = _run_poisoned(q, k, v, True, scale_of(128))
     rows = sample_rows(S, 24, tile_edges=(128, 256))
     bh = list(range(B * H))
     ref_o, ref_l = oracle_on(q, k, v, True, scale_of(128), bh_idx=bh, row_idx=rows)
@@ -259,7 +274,7 @@ def test_resident_grid_edge_items(B, H, S, D, causal, scale):
     scale = scale_of(D) if scale is None else scale
     case(f"bf16 {B}x{H}x{S}x{D} causal={causal} scale={scale}, resident grid")
     q, k, v = device_inputs(B, H, S, D, seed=S + D)
-    o, lse = run_fwd(q, k, v, causal=causal, scale=scale)
+    o, lse = _run_poisoned(q, k, v, causal, scale)
     rows = np.arange(S) if S <= 256 else sample_rows(S, 16, tile_edges=(128, 256))
     bh = list(range(B * H))
     ref_o, ref_l = oracle_on(q, k, v, causal, scale, bh_idx=bh, row_idx=rows)

@@ -69,3 +69,15 @@ def test_m0_is_only_the_lds_copy_destination(device_asm):
                 assert body[k + 1].startswith("global_load_lds_dwordx4"), f"{name}: M0 write not followed by a copy"
             if ins.startswith("global_load_lds_dwordx4"):
                 assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", body[k - 1]), f"{name}: copy without its M0 write"
+
+
+def test_copy_base_is_not_sign_extended(device_asm):
+    """The copies take a wave-uniform 64-bit tile address in SGPRs, rebuilt from
+    two readfirstlane results.  readfirstlane yields a signed 32-bit value: widened
+    without a cast to unsigned, the low word is sign-extended (s_bfe_i64) and an
+    address whose bit 31 is set gets an all-ones high word, which faults.  No
+    kernel that issues copies may sign-extend a 64-bit scalar."""
+    for name, body in _kernels(device_asm):
+        if any(i.startswith("global_load_lds_dwordx4") for i in body):
+            bad = [i for i in body if i.startswith("s_bfe_i64") or i.startswith("s_sext_i32")]
+            assert not bad, f"{name}: sign extension of a scalar: {bad[:3]}"

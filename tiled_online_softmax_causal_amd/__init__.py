@@ -109,12 +109,15 @@ def kernel_name(variant: int, D: int, causal: bool, balanced: bool = False) -> s
 
 def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, S: int,
                D: int, causal: bool, scale: float, dtype: int, stream: int = 0,
-               variant: int = FA_VARIANT_AUTO) -> int:
-    """Call fa_fwd_variant with raw device addresses; returns the fa_status code."""
+               variant: int | None = None) -> int:
+    """Call fa_fwd (``variant`` None) or fa_fwd_variant with raw device addresses;
+    returns the fa_status code."""
     lib = load_library()
-    return lib.fa_fwd_variant(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None,
-                              lse_ptr or None, B, H, S, D, int(bool(causal)), float(scale), dtype,
-                              int(variant), stream or None)
+    args = (q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None, lse_ptr or None, B, H, S, D,
+            int(bool(causal)), float(scale), dtype)
+    if variant is None:
+        return lib.fa_fwd(*args, stream or None)
+    return lib.fa_fwd_variant(*args, int(variant), stream or None)
 
 
 def fa_fwd_ws_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, S: int,
@@ -155,13 +158,15 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
     ``workspace`` (a device tensor of at least ``fwd_workspace_bytes()``
     bytes) the call goes through fa_fwd_ws (run-time balancing of the last
     work items across XCDs; the same results), and ``variant`` must be auto.
+    Otherwise the automatic variant goes through fa_fwd and an explicit one
+    through fa_fwd_variant.
     """
     import torch
 
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share one [B, H, S, D] shape")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be device tensors")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be device tensors on one device")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
     dtype = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_FP32}.get(q.dtype)
@@ -175,12 +180,14 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous device tensor like q")
+    elif (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous device tensor like q, on q's device")
     if return_lse and lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 [B, H, S] tensor")
+    if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or not lse.is_cuda or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 [B, H, S] device tensor on q's device")
     if isinstance(variant, str):
         variant = VARIANTS[variant]
     if stream is None:
@@ -190,15 +197,15 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
         if workspace is not None:
             if variant != FA_VARIANT_AUTO:
                 raise ValueError("a workspace call runs the automatic variant")
-            if not workspace.is_cuda or not workspace.is_contiguous():
-                raise ValueError("workspace must be a contiguous device tensor")
+            if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
+                raise ValueError("workspace must be a contiguous device tensor on q's device")
             status = fa_fwd_ws_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    lse.data_ptr() if lse is not None else 0, B, H, S, D, causal, scale,
                                    dtype, workspace.data_ptr(), workspace.numel() * workspace.element_size(), st)
         else:
             status = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 lse.data_ptr() if lse is not None else 0, B, H, S, D, causal, scale,
-                                dtype, st, variant)
+                                dtype, st, None if variant == FA_VARIANT_AUTO else variant)
     _check(status)
     return (out, lse) if return_lse else out
 
@@ -231,8 +238,9 @@ def dense_fwd(q, k, v, causal: bool = True, scale: float | None = None, workspac
 
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share one [B, H, S, D] shape")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
-        raise ValueError("q, k, v must be bf16 device tensors")
+    if (not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device)
+            or not (q.dtype == k.dtype == v.dtype == torch.bfloat16)):
+        raise ValueError("q, k, v must be bf16 device tensors on one device")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -243,6 +251,8 @@ def dense_fwd(q, k, v, causal: bool = True, scale: float | None = None, workspac
     if workspace is None:
         n = B * H if max_workspace_bytes is None else max(1, min(B * H, max_workspace_bytes // per_head))
         workspace = torch.empty(n * per_head, dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor on q's device")
     out = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     if stream is None:
@@ -285,18 +295,21 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, wo
     ts = (("q", q), ("k", k), ("v", v), ("o", o), ("do", do))
     if q.dim() != 4 or any(t.shape != q.shape for _, t in ts):
         raise ValueError("q, k, v, o, do must share one [B, H, S, D] shape")
-    if any(not t.is_cuda or t.dtype != torch.bfloat16 for _, t in ts):
-        raise ValueError("q, k, v, o, do must be bf16 device tensors")
+    if any(not t.is_cuda or t.dtype != torch.bfloat16 or t.device != q.device for _, t in ts):
+        raise ValueError("q, k, v, o, do must be bf16 device tensors on one device")
     for name, t in ts:
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     B, H, S, D = q.shape
-    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous fp32 [B, H, S] device tensor")
+    if (lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda
+            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 [B, H, S] device tensor on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if workspace is None:
         workspace = torch.empty(B * H * S, dtype=torch.float32, device=q.device)
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     if stream is None:

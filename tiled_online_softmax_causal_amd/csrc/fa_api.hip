@@ -5,8 +5,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "fa_bwd.h"
 #include "fa_dense.h"
@@ -91,6 +93,47 @@ int device_cus() {
   return cus[dev];
 }
 
+// The schedule of the ping-pong grid (fa_schedule.h).  With more items than
+// CUs the grid is resident (one workgroup per CU walking a static list).  The
+// list order is the head-major snake unless the block-major one models at
+// least 3% less time for the busiest workgroup: head-major keeps an XCD's
+// workgroups on fewer heads' K/V at once.  The choice is cached per shape.
+fa::sched::Plan make_plan(int64_t BH, int64_t n_qb, int64_t grid, int64_t S, int causal, int BK, bool balanced) {
+  namespace sc = fa::sched;
+  const int64_t n_items = BH * n_qb;
+  sc::Plan p{sc::kOne, (int)grid, (int)n_qb, (int)BH, 0};
+  if (grid >= n_items) return p;
+  const bool grouped = BH % kNumXcd == 0 && grid % kNumXcd == 0;
+  const int hx = (int)(BH / kNumXcd);
+  p.hs = grouped ? hx : 0;
+  // The order is chosen on the full static lists, the same with or without the
+  // balanced schedule's pool.
+  struct Key {
+    int64_t BH, n_qb, grid, S;
+    int causal, BK, grouped, pad;
+  };
+  thread_local Key last{-1, 0, 0, 0, 0, 0, 0, 0};
+  thread_local int last_order = sc::kXcdHead;
+  const Key key{BH, n_qb, grid, S, causal, BK, grouped, 0};
+  if (std::memcmp(&key, &last, sizeof key) == 0) {
+    p.order = last_order;
+  } else {
+    // per-item overhead: about 2.3 key tiles of 128 keys
+    const double item_cost = 2.3 * 128.0 / BK;
+    sc::Plan head = p, block = p;
+    head.order = grouped ? sc::kXcdHead : sc::kFlatHead;
+    block.order = grouped ? sc::kXcdBlock : sc::kFlatBlock;
+    const double th = sc::plan_makespan(head, (int)S, fa::pp::kBQ, BK, causal != 0, item_cost);
+    const double tb = sc::plan_makespan(block, (int)S, fa::pp::kBQ, BK, causal != 0, item_cost);
+    p.order = tb < 0.97 * th ? block.order : head.order;
+    last = key;
+    last_order = p.order;
+  }
+  // the balanced schedule pools the last eighth of each XCD's heads
+  if (balanced) p.hs = hx - std::max(1, hx / 8);
+  return p;
+}
+
 // The ping-pong kernel holds a whole CU (LDS), so with more work items than
 // CUs it runs resident: one workgroup per CU walking its items, instead of a
 // grid of one workgroup per item that the dispatcher refills as they finish.
@@ -104,30 +147,30 @@ hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o,
   const int64_t n_items = BH * n_qb;
   const int cus = device_cus();
   const int64_t grid = cus >= 8 && n_items > cus ? cus : n_items;
-  const int xcd_group = (BH % kNumXcd) == 0;
   // balanced: a resident grid over whole XCDs with at least 8 heads per XCD
-  const bool balanced = sched && xcd_group && grid < n_items && grid % kNumXcd == 0 &&
+  const bool balanced = sched && BH % kNumXcd == 0 && grid < n_items && grid % kNumXcd == 0 &&
                         grid <= fa::pp::kSchedMaxGrid && BH >= 8 * kNumXcd;
+  const fa::sched::Plan plan = make_plan(BH, n_qb, grid, S, causal, BK, balanced);
   const float c = scale * kLog2e;  // the kernel takes a scale of either sign
   const auto* Q = static_cast<const uint16_t*>(q);
   const auto* K = static_cast<const uint16_t*>(k);
   const auto* V = static_cast<const uint16_t*>(v);
   auto* O = static_cast<uint16_t*>(o);
   const dim3 g((unsigned)grid), b(fa::pp::kThreads);
-  const int s = (int)S, nq = (int)n_qb, ni = (int)n_items;
+  const int s = (int)S;
   if (balanced) {
     if (causal)
-      hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true, true>), g, b, 0, stream, Q, K, V, O, lse, s, nq, ni,
-                         c, xcd_group, sched);
+      hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true, true>), g, b, 0, stream, Q, K, V, O, lse, s, c, plan,
+                         sched);
     else
-      hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false, true>), g, b, 0, stream, Q, K, V, O, lse, s, nq, ni,
-                         c, xcd_group, sched);
+      hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false, true>), g, b, 0, stream, Q, K, V, O, lse, s, c, plan,
+                         sched);
   } else if (causal) {
-    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true, false>), g, b, 0, stream, Q, K, V, O, lse, s, nq, ni,
-                       c, xcd_group, nullptr);
+    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, true, false>), g, b, 0, stream, Q, K, V, O, lse, s, c, plan,
+                       nullptr);
   } else {
-    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false, false>), g, b, 0, stream, Q, K, V, O, lse, s, nq, ni,
-                       c, xcd_group, nullptr);
+    hipLaunchKernelGGL((fa::pp::attn_fwd_pingpong<D, BK, false, false>), g, b, 0, stream, Q, K, V, O, lse, s, c, plan,
+                       nullptr);
   }
   return hipGetLastError();
 }

@@ -56,64 +56,6 @@ __device__ __forceinline__ int swz(int row) {
   return (((row & 3) << 2) | ((row >> 2) & 3)) & (CHUNKS - 1);
 }
 
-// Workgroup id -> (bh, query block).  Heaviest query blocks first (under the
-// causal rule block qb visits qb+1 key ranges).  When the head count is a
-// multiple of 8, every query block of a head is placed on one XCD (workgroups
-// are dispatched round-robin over the 8 XCDs), so the head's K/V stream is
-// shared in that XCD's L2 by the blocks running there at the same time.
-__device__ __forceinline__ void schedule_block(int wg, int n_qb, int xcd_group, int& bh, int& qb) {
-  if (xcd_group) {
-    const int xcd = wg & 7, idx = wg >> 3;
-    bh = (idx / n_qb) * 8 + xcd;
-    qb = n_qb - 1 - idx % n_qb;
-  } else {
-    bh = wg / n_qb;
-    qb = n_qb - 1 - wg % n_qb;
-  }
-}
-
-// The k-th work item (bh, query block) of workgroup w in a grid of G
-// workgroups over n_items = (heads) x n_qb items; false once w has none left.
-// With one item per workgroup (G >= n_items) this is schedule_block.  With
-// fewer, resident workgroups (one per CU), each walks a static sequence:
-// when heads are grouped per XCD (G a multiple of 8), the P = G/8 workgroups
-// of an XCD take the XCD's items P at a time in the heaviest-first order, the
-// order reversed every other round ("snake"), so that over two rounds every
-// workgroup gets about the same work and the workgroups of an XCD stay on
-// the same or adjacent heads, sharing their K/V in that XCD's L2.  That
-// head-major order balances only when a head's n_qb items fill whole rounds
-// (n_qb a multiple of P); otherwise rounds straddle heads, and a workgroup can
-// draw the heaviest block of two heads twice (twice the mean work at
-// S = 7723, b1 h32).  With fewer than P heads per XCD the order is then
-// block-major instead: the XCD's heads take each query-block level in turn,
-// so every round holds items of near-equal weight.
-__device__ __forceinline__ bool next_item(int w, int k, int G, int n_qb, int n_items, int xcd_group, int& bh,
-                                          int& qb) {
-  if (G >= n_items) {
-    if (k > 0) return false;
-    schedule_block(w, n_qb, xcd_group, bh, qb);
-    return true;
-  }
-  if (xcd_group && (G & 7) == 0) {
-    const int P = G >> 3, xcd = w & 7, j = w >> 3;
-    const int idx = P * k + ((k & 1) ? P - 1 - j : j);
-    const int per_xcd = n_items >> 3;
-    if (idx >= per_xcd) return false;
-    const int hx = per_xcd / n_qb;  // heads per XCD
-    const bool block_major = n_qb % P != 0 && hx < P;
-    const int div = block_major ? hx : n_qb, a = idx / div, r = idx - a * div;
-    // wave-uniform; kept in SGPRs (the division is expanded on the vector unit)
-    bh = __builtin_amdgcn_readfirstlane((block_major ? r : a) * 8 + xcd);
-    qb = __builtin_amdgcn_readfirstlane(n_qb - 1 - (block_major ? a : r));
-    return true;
-  }
-  const int item = w + G * k;
-  if (item >= n_items) return false;
-  bh = item / n_qb;
-  qb = n_qb - 1 - item % n_qb;
-  return true;
-}
-
 // Start one 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane
 // l's 16 bytes land at lds_dst + 16*l (lds_dst is wave-uniform).  Issued from
 // inline assembly so that the compiler does not track it: it would otherwise
@@ -143,6 +85,13 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 // 64-bit address.
 __device__ __forceinline__ void copy16_to_lds(const void* base, unsigned voff, char* lds_dst) {
   const unsigned dst = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds_dst;
+  // the base is wave-uniform by contract; readfirstlane states it to the
+  // compiler, so that it is in SGPRs whatever the compiler proved about it
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  // (readfirstlane yields an int: widen through unsigned, never sign-extend)
+  const uint64_t sb = ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) << 32) |
+                      (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
+  base = (const void*)(uintptr_t)sb;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see the comment above
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(dst), "v"(voff), "s"(base) : "m0");

@@ -53,14 +53,15 @@
 // core.
 //
 // Softmax.  Base 2: c = scale*log2(e) (of either sign) is folded into one FMA
-// per score and exp is v_exp_f32.  The maximum only guards exp2 against overflow, so it is
-// maintained lazily: the first tile sets it exactly, later tiles exponentiate
-// against the running value at once, and only if some row's tile sum passes
-// 2^64 is the tile redone with the exact maximum (its scores recomputed from
-// the K tile still in LDS) and the accumulator and sum rescaled.  Numerator
-// and denominator share the running maximum, so the result is that of the
-// exact update up to rounding; probabilities below it underflow as they
-// would against the true one.  The bf16 probabilities are written over the
+// per score and exp is v_exp_f32.  The maximum only guards exp2 against
+// overflow, so it is maintained lazily: an item starts it at the score of a
+// key every row sees (key 0), every tile exponentiates against the running
+// value at once, and only if some row's tile sum passes 2^64 is the tile
+// redone with the exact maximum (its scores recomputed from the K tile still
+// in LDS) and the accumulator and sum rescaled.  Numerator and denominator
+// share the running value, so the result is that of the exact update up to
+// rounding; a probability underflows only where it would also underflow
+// against the true maximum.  The bf16 probabilities are written over the
 // fp32 scores they come from.  The denominator is an fp32 sum of the fp32
 // probabilities; only the P.V operand is rounded to bf16.
 #pragma once
@@ -72,6 +73,7 @@
 #include <utility>
 
 #include "fa_common.h"
+#include "fa_schedule.h"
 
 namespace fa {
 namespace pp {
@@ -144,8 +146,8 @@ __device__ __forceinline__ void schedule_matrix_phase(std::integer_sequence<int,
 template <int D, int BK, bool CAUSAL, bool BALANCED>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int S, int n_qb, int n_items, float c_log2,
-    int xcd_group, unsigned* __restrict__ sched) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int S, float c_log2, fa::sched::Plan plan,
+    unsigned* __restrict__ sched) {
   using G = Geo<D, BK>;
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -180,6 +182,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     int bh, qb, n_tiles, k;
     bool valid;
   };
+  const int n_qb = plan.n_qb;
   //
   // Balanced schedule (a resident grid of G = 8P workgroups, heads grouped per
   // XCD, at least 8 heads per XCD).  Each XCD runs at its own clock under load,
@@ -198,26 +201,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
   // sched: 8 front/back counters 128 bytes apart, a done count, then one
   // (bh, qb) slot per workgroup.  The counters start at zero, and the last
   // workgroup to finish zeroes them again for the next call.
-  const int hx = n_items / (8 * n_qb);           // heads per XCD
-  const int hp = BALANCED ? max(1, hx / 8) : 0;  // of them in the pool
-  const int pool_base = (hx - hp) * n_qb;        // the XCD's static items come before it
   auto make_item = [&](int b, int q, int k) -> Item {
     const int kv_end = CAUSAL ? min(S, q * kBQ + kBQ) : S;
     return Item{b, q, (kv_end + BK - 1) / BK, k, true};
   };
-  // the k-th item of this workgroup's static list: in the balanced schedule
-  // the snake order over the XCD's items in front of its pool
+  // the k-th item of this workgroup's static list (fa_schedule.h); in the
+  // balanced schedule the list covers the XCD's heads in front of its pool and
+  // is one of the two XCD orders (a smaller function: fewer live registers)
   auto static_item = [&](int k) -> Item {
     int b = 0, q = 0;
-    if constexpr (BALANCED) {
-      const int p = (int)gridDim.x >> 3, j = blockIdx.x >> 3;
-      const int idx = p * k + ((k & 1) ? p - 1 - j : j);
-      if (idx >= pool_base) return Item{0, 0, 1, k, false};
-      b = (idx / n_qb) * 8 + (blockIdx.x & 7);
-      q = n_qb - 1 - idx % n_qb;
-    } else if (!next_item(blockIdx.x, k, gridDim.x, n_qb, n_items, xcd_group, b, q)) {
+    if (BALANCED ? !fa::sched::static_item_xcd(plan, blockIdx.x, k, b, q)
+                 : !fa::sched::static_item(plan, blockIdx.x, k, b, q))
       return Item{0, 0, 1, k, false};
-    }
     return make_item(b, q, k);
   };
   // The next pool item for this workgroup (-1 when every pool is empty).  One
@@ -230,18 +225,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     if (wave == 0 && lane_id() == 0) {
       const int x = blockIdx.x & 7;
       int b = -1, q = 0;
-      const int len = hp * n_qb;  // pool position i: head i / n_qb of the pool, block n_qb - 1 - i % n_qb
+      const int len = fa::sched::pool_len(plan);
       for (int d = 0; d < 8 && b < 0; ++d) {
         const int y = (x + d) & 7;
         const unsigned long long old = __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(&sched[32 * y]),
                                                               d == 0 ? 1ull : 1ull << 32, __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT);
         const int front = (int)(unsigned)old, back = (int)(unsigned)(old >> 32);
-        if (front + back < len) {
-          const int i = d == 0 ? front : len - 1 - back;
-          b = (hx - hp + i / n_qb) * 8 + y;
-          q = n_qb - 1 - i % n_qb;
-        }
+        if (front + back < len) fa::sched::pool_item(plan, y, d == 0 ? front : len - 1 - back, b, q);
       }
       __hip_atomic_store(slot, (unsigned)b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(slot + 1, (unsigned)q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -529,12 +520,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           if constexpr (COPIES) copy_at(ks);
         }
       };
-      // The first tile sets the running maximum exactly.  Later tiles
-      // exponentiate against it at once; only if some row's tile sum then passes
-      // 2^64 (a score about 58 above the running maximum, base 2) is the tile
-      // redone: its scores, which the probabilities have overwritten, are
-      // recomputed from K_T (still in its LDS slot: K_{T+3} is copied two phases
-      // later), the maximum is taken exactly, and O and l are rescaled.
+      // The running maximum only guards exp2 against overflow.  An item starts
+      // it at the scaled score of key 0, which every row sees (keys 0 and 4 in
+      // the two half-waves), and every tile exponentiates against it at once;
+      // only if some row's tile sum then passes 2^64 (a score about 64 above
+      // the running value, base 2) is the tile redone: its scores, which the
+      // probabilities have overwritten, are recomputed from K_T (still in its
+      // LDS slot: K_{T+3} is copied two phases later), the maximum is taken
+      // exactly, and O and l are rescaled.
       // (the maximum of the scaled scores: the scale may be negative)
       auto take_exact_max = [&]() {
         float mxk[KB];  // one three-input max chain per 32-key block
@@ -554,9 +547,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
         for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         m_run = m_new;
       };
-      if (t == 0) take_exact_max();
+      // item start: O and l are zero, so no rescale
+      if (t == 0) m_run = max_halves(sacc[0][0] * c_t);
       exponentiate(T_{});
-      if (t > 0 && __builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
+      if (__builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
         if (next_q) load_q(it);
         const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(T) * G::kTileBytes);
 #pragma unroll
