@@ -128,6 +128,34 @@ fa_status fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float 
 /* Workspace bytes fa_fwd_ws needs (a constant, 8192).  Host-only. */
 int64_t fa_fwd_workspace_bytes(void);
 
+/*
+ * fa_fwd_noalloc -- fa_fwd_ws for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments as fa_fwd; the same
+ * results as fa_fwd_ws (and fa_fwd), bit for bit.
+ *
+ * The scheduling workspace is the library's own: one file-scope array of
+ * 8192 bytes per device (the fa_fwd_ws workspace, up to 880 workgroups of
+ * balanced schedule; a device with more compute units runs the static
+ * schedule instead), held until the process ends.  It serves every problem
+ * size, so no size is rejected for it.  The call allocates nothing and calls
+ * no allocating routine.  At the first call on a device, with that device
+ * current, it looks up the array's address and clears it with a fill kernel
+ * on `stream` (stream-ordered, and capturable, unlike a memset); every call
+ * leaves the counters zero again.
+ *
+ * All calls on one device share that array: calls that may overlap on one
+ * device (different streams, or graphs replayed concurrently) race and give
+ * wrong results.  Order them on one stream.
+ *
+ * Returns what fa_fwd returns; FA_ERR_HIP also if the array's address cannot
+ * be obtained (fa_last_hip_error() has the code).  A call rejected for its
+ * arguments enqueues nothing.
+ */
+fa_status fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                         int64_t H, int64_t S, int64_t D, int causal, float scale, fa_dtype dtype,
+                         void *stream);
+
 /* The variant fa_fwd would run for this shape (an fa_variant value), or -1
  * if the arguments are unsupported.  Host-only; touches no device. */
 int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype);

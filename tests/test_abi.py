@@ -194,3 +194,16 @@ def test_fwd_ws_rejects_before_launch():
     assert _fwd_ws(scale=float("inf")) == fa.FA_ERR_INVALID_ARGUMENT
     assert _fwd_ws(D=48) == fa.FA_ERR_UNSUPPORTED
     assert _fwd_ws(dtype=7) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_noalloc_validates_on_the_host():
+    """fa_fwd_noalloc checks its arguments before it touches the device (its
+    scratch is looked up only for a valid call), so these run without a GPU."""
+    P = 1 << 20
+    assert fa.fa_fwd_noalloc_raw(0, P, P, P, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_fwd_noalloc_raw(P, P, P, P, 0, 0, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_fwd_noalloc_raw(P, P, P, P, 0, 1, 1, 64, 128, True, float("inf"),
+                                 fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_fwd_noalloc_raw(P, P, P, P, 0, 1, 1, 64, 24, True, 0.1, fa.FA_DTYPE_BF16) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_noalloc_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, 7) == fa.FA_ERR_UNSUPPORTED
+    assert fa.load_library().fa_last_hip_error() == 0

@@ -22,7 +22,7 @@ FA_VARIANT_AUTO, FA_VARIANT_MFMA_B256, FA_VARIANT_MFMA_B128, FA_VARIANT_VALU, FA
 VARIANTS = {"auto": 0, "mfma_b256": 1, "mfma_b128": 2, "valu": 3, "mfma_b256_k128": 4}
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_ws", "fa_fwd_workspace_bytes", "fa_fwd_variant", "fa_fwd_select_variant",
+EXPORTS = ("fa_fwd", "fa_fwd_ws", "fa_fwd_workspace_bytes", "fa_fwd_noalloc", "fa_fwd_variant", "fa_fwd_select_variant",
            "fa_fwd_tiles_per_head",
            "fa_dense_fwd", "fa_dense_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_status_str", "fa_last_hip_error", "fa_version")
@@ -49,6 +49,8 @@ def load_library(path: str = LIBRARY_PATH):
     lib.fa_fwd.restype = i32
     lib.fa_fwd_ws.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, p, i64, p]
     lib.fa_fwd_ws.restype = i32
+    lib.fa_fwd_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, p]
+    lib.fa_fwd_noalloc.restype = i32
     lib.fa_fwd_workspace_bytes.argtypes = []
     lib.fa_fwd_workspace_bytes.restype = i64
     lib.fa_fwd_variant.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, f32, i32, i32, p]
@@ -128,6 +130,15 @@ def fa_fwd_ws_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, 
     return lib.fa_fwd_ws(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None, lse_ptr or None,
                          B, H, S, D, int(bool(causal)), float(scale), dtype, ws_ptr or None, ws_bytes,
                          stream or None)
+
+
+def fa_fwd_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, S: int,
+                       D: int, causal: bool, scale: float, dtype: int, stream: int = 0) -> int:
+    """Call fa_fwd_noalloc (the library's own scheduling scratch) with raw device
+    addresses; returns the fa_status code."""
+    lib = load_library()
+    return lib.fa_fwd_noalloc(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None, lse_ptr or None,
+                              B, H, S, D, int(bool(causal)), float(scale), dtype, stream or None)
 
 
 def fwd_workspace_bytes() -> int:

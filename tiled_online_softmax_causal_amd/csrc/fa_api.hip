@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "fa_bwd.h"
 #include "fa_dense.h"
@@ -282,10 +283,10 @@ int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant) {
 
 namespace {
 
-// The forward with a given variant; sched is the balanced schedule's workspace or NULL.
-fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                   int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, int variant, unsigned* sched,
-                   void* stream) {
+// Host-side checks of a forward call (nothing is enqueued); on success the
+// variant to run (AUTO resolved) is stored in *variant.
+fa_status validate_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int64_t B,
+                       int64_t H, int64_t S, int64_t D, float scale, fa_dtype dtype, int* variant) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARGUMENT;
   if (B < 1 || H < 1 || S < 1 || D < 1) return FA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
@@ -295,12 +296,21 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   // in-kernel offsets within one head are 32-bit; the grid is one dimension
   if (S * D >= (int64_t(1) << 31) || B > INT32_MAX / H) return FA_ERR_UNSUPPORTED;
-  if (variant == FA_VARIANT_AUTO) variant = select_variant(B, H, S, D, dtype);
-  if (!variant_covers(variant, D, dtype)) return FA_ERR_UNSUPPORTED;
-  const int64_t BH = B * H;
-  const int64_t bq = variant == FA_VARIANT_VALU ? fa::kValuBQ : mfma_block_q(variant);
-  if (BH * ceil_div(S, bq) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  int var = *variant == FA_VARIANT_AUTO ? select_variant(B, H, S, D, dtype) : *variant;
+  if (!variant_covers(var, D, dtype)) return FA_ERR_UNSUPPORTED;
+  const int64_t bq = var == FA_VARIANT_VALU ? fa::kValuBQ : mfma_block_q(var);
+  if (B * H * ceil_div(S, bq) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  *variant = var;
+  return FA_OK;
+}
 
+// The forward with a given variant; sched is the balanced schedule's workspace or NULL.
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, int variant, unsigned* sched,
+                   void* stream) {
+  const fa_status valid = validate_fwd(q, k, v, o, lse, B, H, S, D, scale, dtype, &variant);
+  if (valid != FA_OK) return valid;
+  const int64_t BH = B * H;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (variant == FA_VARIANT_VALU) {
@@ -321,6 +331,47 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
     return FA_ERR_HIP;
   }
   return FA_OK;
+}
+
+}  // namespace
+
+// The allocation-free entry point's scheduling scratch: one 8 KB array per
+// device, at file scope, held until the process ends.  Host code never uses
+// its name as an address: the device address comes from hipGetSymbolAddress,
+// once per device, with that device current.
+__device__ __align__(256) unsigned scratch[fa::pp::kSchedBytes / 4];
+
+namespace {
+
+__global__ void zero_words(unsigned* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+unsigned* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address; at the first call on a device it is
+// looked up and cleared by a fill kernel on `stream` (stream-ordered, and a
+// kernel rather than a memset, so a caller may capture it in a graph).
+hipError_t device_scratch(hipStream_t stream, unsigned** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(zero_words, dim3(1), dim3(256), 0, stream, static_cast<unsigned*>(p),
+                       fa::pp::kSchedBytes / 4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<unsigned*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -346,6 +397,20 @@ fa_status fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float*
   if (!workspace || !aligned(workspace, 8) || workspace_bytes < fa::pp::kSchedBytes) return FA_ERR_INVALID_ARGUMENT;
   return fwd_impl(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, FA_VARIANT_AUTO,
                   static_cast<unsigned*>(workspace), stream);
+}
+
+fa_status fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                         int64_t S, int64_t D, int causal, float scale, fa_dtype dtype, void* stream) {
+  int variant = FA_VARIANT_AUTO;
+  const fa_status valid = validate_fwd(q, k, v, o, lse, B, H, S, D, scale, dtype, &variant);
+  if (valid != FA_OK) return valid;  // a rejected call enqueues nothing, not even the scratch's first clear
+  unsigned* ws = nullptr;
+  const hipError_t e = device_scratch(static_cast<hipStream_t>(stream), &ws);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  return fwd_impl(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, FA_VARIANT_AUTO, ws, stream);
 }
 
 int64_t fa_dense_workspace_bytes(int64_t S) { return S < 1 ? 0 : fa::dense::head_bytes(S); }
