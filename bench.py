@@ -70,9 +70,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None if the
-    kernel sources changed since the counters were taken."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3
+    counter runs, or None if the kernel sources changed since the counters were
+    taken or the counters are for another kernel (another schedule or variant)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -81,16 +82,23 @@ def measured_traffic(workload: str):
     entry = rec.get("workloads", {}).get(workload)
     if not entry or rec.get("source_sha256") != kernel_source_hash():
         return None
+    if not str(entry.get("kernel", "")).startswith(kernel):
+        return None
     return entry.get("hbm_bytes_per_launch")
 
 
-def _counter_mean(csv_path: str, counter: str, kernel_substr: str) -> float:
+def _counter_mean(csv_path: str, counter: str, kernel_substr: str):
+    """Mean of `counter` over the dispatches of the one kernel matching kernel_substr,
+    and that kernel's name (without its argument list)."""
     import csv
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+    rows = [r for r in csv.DictReader(open(csv_path))
             if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
-    if not vals:
+    if not rows:
         raise SystemExit(f"no {counter} rows for a kernel matching {kernel_substr!r} in {csv_path}")
-    return sum(vals) / len(vals)
+    names = {r["Kernel_Name"].split("(")[0].replace("void ", "").strip() for r in rows}
+    if len(names) != 1:
+        raise SystemExit(f"several kernels match {kernel_substr!r} in {csv_path}: {sorted(names)}")
+    return sum(float(r["Counter_Value"]) for r in rows) / len(rows), names.pop()
 
 
 def record_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
@@ -102,10 +110,12 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv
     The result is stored with a hash of the kernel sources, so it is reported only
     while the kernel is unchanged.
     """
-    fetch_kib = _counter_mean(fetch_csv, "FETCH_SIZE", "attn_fwd")
-    write_kib = _counter_mean(write_csv, "WRITE_SIZE", "attn_fwd")
-    copy_fetch_kib = _counter_mean(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
-    copy_write_kib = _counter_mean(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    fetch_kib, kernel = _counter_mean(fetch_csv, "FETCH_SIZE", "attn_fwd")
+    write_kib, kernel_w = _counter_mean(write_csv, "WRITE_SIZE", "attn_fwd")
+    if kernel_w != kernel:
+        raise SystemExit(f"the counter runs are of different kernels: {kernel} / {kernel_w}")
+    copy_fetch_kib, _ = _counter_mean(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    copy_write_kib, _ = _counter_mean(copy_write_csv, "WRITE_SIZE", "copyBuffer")
     true_kib = copy_mib * 1024.0
     f_fetch, f_write = true_kib / copy_fetch_kib, true_kib / copy_write_kib
     hbm = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
@@ -117,6 +127,7 @@ def record_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv
     if rec.get("source_sha256") != kernel_source_hash():
         rec = {"source_sha256": kernel_source_hash(), "workloads": {}}
     rec["workloads"][workload] = {
+        "kernel": kernel,
         "hbm_bytes_per_launch": round(hbm),
         "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
         "copy_calibration": {"mib": copy_mib, "fetch_kib": copy_fetch_kib, "write_kib": copy_write_kib,
@@ -156,6 +167,7 @@ def cpu_baseline(q, k, v, o, lse, n_heads: int, causal: bool, scale: float):
     parity["ok"] = (parity["o_max_abs"] <= 1e-2 and parity["o_mean_abs"] <= 1e-3
                     and parity["lse_max_abs"] <= 1e-3)
     base = {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(),
             "sample": f"{n_heads} of {B * H} (batch, head) pairs, all {S} rows each "
                       f"({flops / 1e9:.1f} GFLOP fp64), {secs:.2f} s",
             "seconds": secs}
@@ -267,7 +279,7 @@ def main():
         f"{achieved:.1f} TFLOP/s = {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak, "
         f"{nbytes / (kernel_ms * 1e-3) / 1e9:.1f} GB/s effective")
 
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, fa.kernel_name(variant, D, causal, balanced))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": fa.kernel_name(variant, D, causal, balanced), "kernel_ms": round(kernel_ms, 5),
@@ -307,12 +319,28 @@ def main():
                           "effective_hbm_gbs": round(nbytes / (cold_ms * 1e-3) / 1e9, 1)}
         log(f"[bench] cold: median {cold_ms:.4f} ms over {args.steps} launches, "
             f"{result['cold']['effective_hbm_gbs']} GB/s effective")
+    # One more step after the timed ones, into outputs filled with NaN and with
+    # the same workspace: the parity check below reads this step's outputs, so it
+    # shows that a call in the timed configuration computes every row (a skipped
+    # work item would leave NaN), and that the workspace comes back zeroed.
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    step()
+    torch.cuda.synchronize()
+    unwritten = int((~torch.isfinite(o)).sum().item()) + int((~torch.isfinite(lse)).sum().item())
+    ws_clean = True if ws is None else int(ws.count_nonzero().item()) == 0
+    log(f"[bench] poisoned check step: {unwritten} non-finite outputs, workspace zero: {ws_clean}")
+
     if not args.no_cpu_baseline:
         log(f"[bench] oracle on {cpu_heads} whole heads (CPU baseline + parity)")
         base, parity = cpu_baseline(q, k, v, o, lse, cpu_heads, causal, scale)
         log(f"[bench] oracle {base['seconds']:.2f} s on {base['cores']} threads; parity {parity}")
         base.pop("seconds")
         result["cpu_baseline"] = base
+        parity["checked_step"] = "after the timed steps, into NaN-filled outputs, same workspace"
+        parity["non_finite_outputs"] = unwritten
+        parity["workspace_left_zero"] = ws_clean
+        parity["ok"] = parity["ok"] and unwritten == 0 and ws_clean
         result["parity"] = parity
     print(json.dumps(result), flush=True)
 
