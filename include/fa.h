@@ -62,13 +62,18 @@ typedef enum fa_status {
  *   VALU:      fp32 or bf16, D in {16, 32, 64, 128}; one lane per query,
  *              fp32 vector arithmetic (the fp32 path, and small head dims).
  *   MFMA_B256_K128: as MFMA_B256 with 128-key tiles (64-key tiles otherwise):
- *              twice the work per phase, half the barriers, 2-slot rings. */
+ *              twice the work per phase, half the barriers, 2-slot rings.
+ *   SPLIT:     bf16, D in {64, 128}; short sequences: a workgroup of 4 waves
+ *              runs a pair of 64-row query blocks (qb and n-1-qb, equal work
+ *              under the causal rule) with two key streams, merged on chip
+ *              (AUTO picks it when 256-row blocks number fewer than 256). */
 typedef enum fa_variant {
   FA_VARIANT_AUTO = 0,
   FA_VARIANT_MFMA_B256 = 1,
   FA_VARIANT_MFMA_B128 = 2,
   FA_VARIANT_VALU = 3,
-  FA_VARIANT_MFMA_B256_K128 = 4
+  FA_VARIANT_MFMA_B256_K128 = 4,
+  FA_VARIANT_SPLIT = 5
 } fa_variant;
 
 /*

@@ -91,7 +91,10 @@ def test_size_limits_rejected():
 def test_variant_selection():
     bf16, f32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP32
     assert fa.select_variant(8, 32, 8192, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
-    assert fa.select_variant(1, 32, 1024, 128, bf16) == fa.FA_VARIANT_MFMA_B128
+    assert fa.select_variant(1, 32, 1024, 128, bf16) == fa.FA_VARIANT_SPLIT
+    assert fa.select_variant(1, 32, 1792, 128, bf16) == fa.FA_VARIANT_MFMA_B128
+    assert fa.select_variant(1, 16, 1792, 128, bf16) == fa.FA_VARIANT_SPLIT
+    assert fa.select_variant(1, 32, 2048, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     assert fa.select_variant(1, 1, 64, 16, f32) == fa.FA_VARIANT_VALU
     assert fa.select_variant(1, 1, 64, 16, bf16) == fa.FA_VARIANT_VALU
     assert fa.select_variant(1, 1, 64, 128, f32) == fa.FA_VARIANT_VALU
@@ -104,7 +107,8 @@ def test_variant_selection():
 def test_scheduler_tile_counts(S, causal):
     """The library's per-head tile count equals the causal block rule's closed form."""
     for variant, bq, bk in ((fa.FA_VARIANT_MFMA_B256, 256, 64), (fa.FA_VARIANT_MFMA_B256_K128, 256, 128),
-                            (fa.FA_VARIANT_MFMA_B128, 128, 64), (fa.FA_VARIANT_VALU, 64, 32)):
+                            (fa.FA_VARIANT_MFMA_B128, 128, 64), (fa.FA_VARIANT_SPLIT, 64, 128),
+                            (fa.FA_VARIANT_VALU, 64, 32)):
         assert fa.tiles_per_head(S, causal, variant) == causal_kv_tiles(S, bq, bk, causal)
     assert fa.tiles_per_head(S, causal, 0) == 0
 

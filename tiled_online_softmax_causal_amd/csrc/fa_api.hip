@@ -15,6 +15,7 @@
 #include "fa_dense.h"
 #include "fa_fwd_pingpong.h"
 #include "fa_mfma_bf16.h"
+#include "fa_split.h"
 #include "fa_valu.h"
 
 namespace {
@@ -29,16 +30,21 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int64_t mfma_block_q(int variant) {
+  if (variant == FA_VARIANT_SPLIT) return fa::split::kBQ;
   return variant == FA_VARIANT_MFMA_B256 || variant == FA_VARIANT_MFMA_B256_K128 ? fa::pp::kBQ : 4 * 32;
 }
 
-int64_t mfma_block_k(int variant) { return variant == FA_VARIANT_MFMA_B256_K128 ? 128 : fa::kBK; }
+int64_t mfma_block_k(int variant) {
+  if (variant == FA_VARIANT_SPLIT) return fa::split::kBK;
+  return variant == FA_VARIANT_MFMA_B256_K128 ? 128 : fa::kBK;
+}
 
 bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
   switch (variant) {
     case FA_VARIANT_MFMA_B256:
     case FA_VARIANT_MFMA_B128:
     case FA_VARIANT_MFMA_B256_K128:
+    case FA_VARIANT_SPLIT:
       return dtype == FA_DTYPE_BF16 && (D == 64 || D == 128);
     case FA_VARIANT_VALU:
       return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP32) && (D == 16 || D == 32 || D == 64 || D == 128);
@@ -47,13 +53,17 @@ bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
   }
 }
 
-// Shape-only choice: bf16 with D 64/128 runs on the matrix cores, in 256-row
-// workgroups (one per CU) with 128-key tiles unless that leaves CUs idle,
-// where the 128-row variant doubles the grid.
+// Shape-only choice (for the 256 CUs of an MI355X): bf16 with D 64/128 runs
+// on the matrix cores, in 256-row workgroups (one per CU) with 128-key tiles
+// unless that leaves CUs idle (fewer 256-row items than CUs).  Then the split
+// kernel runs pairs of 64-row blocks with four key streams per workgroup, as
+// long as its units (about one per 128 rows of a head) fit on the CUs at once;
+// beyond that the 128-row kernel, two workgroups per CU, balances better.
 int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
   if (dtype == FA_DTYPE_BF16 && (D == 64 || D == 128)) {
-    const int64_t wgs = B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128));
-    return wgs >= 256 ? FA_VARIANT_MFMA_B256_K128 : FA_VARIANT_MFMA_B128;
+    constexpr int64_t kCUs = 256;
+    if (B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128)) >= kCUs) return FA_VARIANT_MFMA_B256_K128;
+    return B * H * ceil_div(S, 2 * fa::split::kBQ) <= kCUs ? FA_VARIANT_SPLIT : FA_VARIANT_MFMA_B128;
   }
   if (variant_covers(FA_VARIANT_VALU, D, dtype)) return FA_VARIANT_VALU;
   return -1;
@@ -176,6 +186,28 @@ hipError_t launch_pingpong(const void* q, const void* k, const void* v, void* o,
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t S,
+                        int causal, float scale, hipStream_t stream) {
+  namespace sp = fa::split;
+  const int64_t n_qb = ceil_div(S, sp::kBQ);
+  const int64_t grid = BH * sp::units_per_head((int)n_qb, causal != 0);
+  const int xcd_group = (BH % kNumXcd) == 0;
+  const float c = std::fabs(scale) * kLog2e;
+  const int negate_q = scale < 0.f;
+  const auto* Q = static_cast<const uint16_t*>(q);
+  const auto* K = static_cast<const uint16_t*>(k);
+  const auto* V = static_cast<const uint16_t*>(v);
+  auto* O = static_cast<uint16_t*>(o);
+  if (causal)
+    hipLaunchKernelGGL((sp::attn_fwd_split<D, true>), dim3((unsigned)grid), dim3(sp::kThreads), 0, stream, Q, K, V,
+                       O, lse, (int)S, (int)n_qb, (int)BH, c, negate_q, xcd_group);
+  else
+    hipLaunchKernelGGL((sp::attn_fwd_split<D, false>), dim3((unsigned)grid), dim3(sp::kThreads), 0, stream, Q, K, V,
+                       O, lse, (int)S, (int)n_qb, (int)BH, c, negate_q, xcd_group);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_valu(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t S,
                        int causal, float scale, hipStream_t stream) {
@@ -261,7 +293,7 @@ int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype d
 int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant) {
   int64_t bq, bk;
   if (variant == FA_VARIANT_MFMA_B256 || variant == FA_VARIANT_MFMA_B128 ||
-      variant == FA_VARIANT_MFMA_B256_K128) {
+      variant == FA_VARIANT_MFMA_B256_K128 || variant == FA_VARIANT_SPLIT) {
     bq = mfma_block_q(variant);
     bk = mfma_block_k(variant);
   } else if (variant == FA_VARIANT_VALU) {
@@ -319,6 +351,9 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   } else if (variant == FA_VARIANT_MFMA_B256_K128) {
     err = D == 128 ? launch_pingpong<128, 128>(q, k, v, o, lse, BH, S, causal, scale, sched, st)
                    : launch_pingpong<64, 128>(q, k, v, o, lse, BH, S, causal, scale, sched, st);
+  } else if (variant == FA_VARIANT_SPLIT) {
+    err = D == 128 ? launch_split<128>(q, k, v, o, lse, BH, S, causal, scale, st)
+                   : launch_split<64>(q, k, v, o, lse, BH, S, causal, scale, st);
   } else if (variant == FA_VARIANT_MFMA_B256) {
     err = D == 128 ? launch_pingpong<128, 64>(q, k, v, o, lse, BH, S, causal, scale, sched, st)
                    : launch_pingpong<64, 64>(q, k, v, o, lse, BH, S, causal, scale, sched, st);
