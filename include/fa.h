@@ -63,10 +63,13 @@ typedef enum fa_status {
  *              fp32 vector arithmetic (the fp32 path, and small head dims).
  *   MFMA_B256_K128: as MFMA_B256 with 128-key tiles (64-key tiles otherwise):
  *              twice the work per phase, half the barriers, 2-slot rings.
- *   SPLIT:     bf16, D in {64, 128}; short sequences: a workgroup of 4 waves
+ *   SPLIT:     bf16, D in {64, 128}; short sequences: a workgroup of 8 waves
  *              runs a pair of 64-row query blocks (qb and n-1-qb, equal work
- *              under the causal rule) with two key streams, merged on chip
- *              (AUTO picks it when 256-row blocks number fewer than 256). */
+ *              under the causal rule), as two 32-row halves times four key
+ *              streams whose partial results are merged on chip.  AUTO picks
+ *              it when the 256-row blocks number fewer than 256 and the pairs
+ *              of 64-row blocks number at most 256; MFMA_B128 in between; and
+ *              MFMA_B256_K128 from 256 blocks of 256 rows on. */
 typedef enum fa_variant {
   FA_VARIANT_AUTO = 0,
   FA_VARIANT_MFMA_B256 = 1,
