@@ -182,6 +182,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     int bh, qb, n_tiles, k;
     bool valid;
   };
+  struct Span {
+    int n_w, t_mask, t_last;
+  };
   const int n_qb = plan.n_qb;
   //
   // Balanced schedule (a resident grid of G = 8P workgroups, heads grouped per
@@ -328,20 +331,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     };
     // The copy cursor walks this group's tensor along the tile sequence; past
     // its end it keeps re-reading the last tile into the next slots, which keeps
-    // the wait counts uniform.
-    Item c_it = cur;
-    int c_t = 0, c_T = 0;
+    // the wait counts uniform.  Within an item it only adds: the tile address,
+    // the rows left before the end of the sequence and the ring slot offset
+    // move by fixed steps (no per-tile multiply or modulo in the softmax wave).
+    const uint16_t* const c_tensor = grp == 0 ? K : V;
+    char* const c_ring = grp == 0 ? kbuf0 : vbuf0;
+    const int c_ring_bytes = (grp == 0 ? G::kStagesK : G::kStagesV) * G::kTileBytes;
+    const uint16_t* c_src = c_tensor + (size_t)cur.bh * S * D;
+    int c_k = cur.k, c_left = cur.n_tiles, c_rows = S, c_slot = 0;
     auto next_copy = [&]() -> Copy {
-      const Copy c{(grp == 0 ? K : V) + (size_t)c_it.bh * S * D + (size_t)c_t * BK * D, S - c_t * BK,
-                   grp == 0 ? kbuf0 + kslot(c_T) * G::kTileBytes : vbuf0 + vslot(c_T) * G::kTileBytes};
-      ++c_T;
-      if (c_t + 1 < c_it.n_tiles) {
-        ++c_t;
+      const Copy c{c_src, c_rows, c_ring + c_slot};
+      c_slot = c_slot + G::kTileBytes == c_ring_bytes ? 0 : c_slot + G::kTileBytes;
+      if (c_left > 1) {
+        --c_left;
+        c_src += BK * D;
+        c_rows -= BK;
       } else {
-        const Item nx = item_at(c_it.k + 1);
+        const Item nx = item_at(c_k + 1);
         if (nx.valid) {
-          c_it = nx;
-          c_t = 0;
+          c_k = nx.k;
+          c_left = nx.n_tiles;
+          c_rows = S;
+          c_src = c_tensor + (size_t)nx.bh * S * D;
         }
       }
       return c;
@@ -355,6 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       const unsigned voff = min(off0 + (unsigned)(i * G::kRowsPerLoad * G::kRowBytes), lim);
       copy16_to_lds(c.tile, voff, c.slot + (i * kGroupThreads + gwave * 64) * 16);
     };
+
     // per-lane read offsets within a tile.  K: row 32*kb + col, logical chunk
     // 2*ds + half.  V (transposed read): rows 16*ks + 4*half + u/4 (+8 for the
     // upper k-slots), logical chunk 4*db + 2*(quad%2) + (u%4)/2, byte 8*(u%2).
@@ -451,38 +463,51 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       l_run = 0.f;
     };
 
+    // Per-item, per-wave tile bounds of the softmax phases: the wave's rows see
+    // keys only in tiles t < n_w (keys below min(S, q0w + 32)); tiles
+    // t >= t_mask straddle the diagonal or run past S and are masked per
+    // element; t_last is the tile in whose phase the next item's Q is loaded
+    // (-1: no next item).
+    auto span_of = [&](const Item& it, const Item& nx) -> Span {
+      const int q0w = it.qb * kBQ + wave * kQW;
+      const int n_w = q0w >= S ? 0 : (CAUSAL ? min(it.n_tiles, (min(q0w + kQW, S) - 1) / BK + 1) : it.n_tiles);
+      const int t_mask = CAUSAL ? min((q0w + 1) / BK, S / BK) : S / BK;
+      return Span{n_w, t_mask, nx.valid ? it.n_tiles - 1 : -1};
+    };
+
     // ---- softmax phase for tile t of item `it` (flattened index T): S -> bf16
     // P, running max / sum.  The NL load steps of copy cp are issued along the
     // way, one per KS / NL exponential steps (pinned there by a scheduling
     // barrier).  When `next_q` is set the next item's Q operand has already been
     // loaded over this item's (its latency hidden by this phase), and the rare
     // recompute below reloads this item's first.
-    auto softmax_phase = [&](const Item& it, int t, int T, const Copy& cp, bool next_q, const Item& nx) {
+    auto softmax_phase = [&](const Item& it, int t, int T, const Copy& cp, bool next_q, const Item& nx,
+                             const Span& sp) {
       const int q0w = it.qb * kBQ + wave * kQW;
-      // tiles this wave takes part in (its rows see keys below min(S, q0w + 32))
-      const int n_w = q0w >= S ? 0 : (CAUSAL ? min(it.n_tiles, (min(q0w + kQW, S) - 1) / BK + 1) : it.n_tiles);
       // the copy offsets are formed here, not hoisted out of the loop, where
       // they would hold registers through the matrix phase
       unsigned off0 = g_off;
       asm volatile("" : "+v"(off0));
-      auto copy_at = [&](int ks) {
-        if (ks % (KS / NL) == 0) {
+      // copy modes: 0 none, 1 the tile's copy steps
+      auto copy_at = [&](int ks, auto mode_c) {
+        if (decltype(mode_c)::value != 0 && ks % (KS / NL) == 0) {
           copy_step(ks / (KS / NL), cp, off0);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      if (t >= n_w) {
+      using Clamped = std::integral_constant<int, 1>;
+      if (t >= sp.n_w) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) set_p(ks, (bf16x8_t){});
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) copy_at(ks);
+        for (int ks = 0; ks < KS; ++ks) copy_at(ks, Clamped{});
         return;
       }
       const int kv0 = t * BK;
       const int qi = q0w + col;
       // Tiles that straddle the diagonal or run past S move to the base-2 domain
       // here, so a hidden score is a plain -inf even when the scale is 0.
-      const bool masked = (CAUSAL && kv0 + BK - 1 > q0w) || kv0 + BK > S;
+      bool masked = t >= sp.t_mask;
       const float c_t = masked ? 1.f : c_log2;
       auto apply_mask = [&]() {
 #pragma unroll
@@ -495,11 +520,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           }
       };
       if (masked) apply_mask();
-      // exponentiate against the running maximum (the copies interleaved when
-      // COPIES); rs is the lane's share of the tile's row sum
+      // exponentiate against the running maximum (the copies interleaved in
+      // copy mode 1); rs is the lane's share of the tile's row sum
       float rs = 0.f;
-      auto exponentiate = [&](auto copies_c) {
-        constexpr bool COPIES = decltype(copies_c)::value;
+      auto exponentiate = [&](auto mode_c) {
         const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
         rs = 0.f;
 #pragma unroll
@@ -510,14 +534,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           for (int e = 0; e < 8; e += 2) {
             const f32x2_t x = {__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e], c_t, neg_m)),
                                __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r0 + e + 1], c_t, neg_m))};
-            rs += x[0];
+            rs = ks == 0 && e == 0 ? x[0] : rs + x[0];
             rs += x[1];
             const bf16x2_t b = __builtin_convertvector(x, bf16x2_t);
             p8[e] = b[0];
             p8[e + 1] = b[1];
           }
           set_p(ks, p8);
-          if constexpr (COPIES) copy_at(ks);
+          copy_at(ks, mode_c);
         }
       };
       // The running maximum only guards exp2 against overflow.  An item starts
@@ -549,8 +573,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       };
       // item start: O and l are zero, so no rescale
       if (t == 0) m_run = max_halves(sacc[0][0] * c_t);
-      exponentiate(T_{});
+      exponentiate(Clamped{});
       if (__builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
+        // the two conditions again, from opaque copies of their bounds, rather
+        // than kept as masks through the exponentials above (this path is rare)
+        int t_last = sp.t_last, t_mask = sp.t_mask;
+        asm volatile("" : "+s"(t_last), "+s"(t_mask));
+        next_q = t == t_last;
+        masked = t >= t_mask;
         if (next_q) load_q(it);
         const char* Kl = kbuf0 + __builtin_amdgcn_readfirstlane(kslot(T) * G::kTileBytes);
 #pragma unroll
@@ -564,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
         if (next_q) load_q(nx);
         if (masked) apply_mask();
         take_exact_max();
-        exponentiate(F_{});
+        exponentiate(std::integral_constant<int, 0>{});
       }
       l_run += rs;
     };
@@ -599,20 +629,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     Item prev = cur;
     int T = 0;
     // the softmax phase of tile t of the current item (flattened index T)
-    auto softmax_step = [&](int t, const Item& nx) {
+    auto softmax_step = [&](int t, const Item& nx, const Span& sp) {
       const Copy cp = next_copy();
       if (t == 0 && T > 0) finish_item(prev);
-      const bool next_q = t + 1 == cur.n_tiles && nx.valid;
+      const bool next_q = t == sp.t_last;
       if (next_q) load_q(nx);
-      softmax_phase(cur, t, T, cp, next_q, nx);
+      softmax_phase(cur, t, T, cp, next_q, nx, sp);
     };
     if (grp == 0) {
       matrix_phase(0);  // phase 0
       phase_barrier();
       for (;;) {
         const Item nx = item_at(cur.k + 1);
+        const Span sp = span_of(cur, nx);
         for (int t = 0; t < cur.n_tiles; ++t, ++T) {
-          softmax_step(t, nx);  // phase 2T + 1
+          softmax_step(t, nx, sp);  // phase 2T + 1
           __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());
           phase_barrier();
           matrix_phase(T + 1);  // phase 2T + 2
@@ -636,8 +667,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       phase_barrier();
       for (;;) {
         const Item nx = item_at(cur.k + 1);
+        const Span sp = span_of(cur, nx);
         for (int t = 0; t < cur.n_tiles; ++t, ++T) {
-          softmax_step(t, nx);  // phase 2T + 2
+          softmax_step(t, nx, sp);  // phase 2T + 2
           phase_barrier();
           matrix_phase(T + 1);  // phase 2T + 3
           __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
