@@ -55,21 +55,23 @@ typedef enum fa_status {
 
 /* Kernel variants.  FA_VARIANT_AUTO picks one from the shape; the others
  * exist so tests can show that results do not depend on the tiling.
- *   MFMA_B256: bf16, D in {64, 128}; 256-row query blocks, 8 waves of 32 rows in
- *              two groups that alternate matrix-core and softmax phases.
+ *   MFMA_B256: bf16, D in {64, 128}, S >= 64; 256-row query blocks, 8 waves of
+ *              32 rows in two groups that alternate matrix-core and softmax
+ *              phases; 64-key tiles, always copied whole (a last tile cut short
+ *              by S is copied as the sequence's last 64 rows, hence S >= 64).
  *   MFMA_B128: bf16, D in {64, 128}; 128-row query blocks, 4 waves of 32 rows,
  *              two workgroups per CU (used when 256-row blocks leave CUs idle).
  *   VALU:      fp32 or bf16, D in {16, 32, 64, 128}; one lane per query,
  *              fp32 vector arithmetic (the fp32 path, and small head dims).
- *   MFMA_B256_K128: as MFMA_B256 with 128-key tiles (64-key tiles otherwise):
- *              twice the work per phase, half the barriers, 2-slot rings.
+ *   MFMA_B256_K128: as MFMA_B256 with 128-key tiles, S >= 128: twice the work
+ *              per phase, half the barriers, 2-slot rings.
  *   SPLIT:     bf16, D in {64, 128}; short sequences: a workgroup of 8 waves
  *              runs a pair of 64-row query blocks (qb and n-1-qb, equal work
  *              under the causal rule), as two 32-row halves times four key
  *              streams whose partial results are merged on chip.  AUTO picks
  *              it when the 256-row blocks number fewer than 256 and the pairs
  *              of 64-row blocks number at most 256; MFMA_B128 in between; and
- *              MFMA_B256_K128 from 256 blocks of 256 rows on. */
+ *              MFMA_B256_K128 from 256 blocks of 256 rows on (and S >= 128). */
 typedef enum fa_variant {
   FA_VARIANT_AUTO = 0,
   FA_VARIANT_MFMA_B256 = 1,
@@ -102,7 +104,8 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
                  void *stream);
 
 /* fa_fwd with an explicit kernel variant (fa_variant); FA_ERR_UNSUPPORTED if
- * that variant does not cover dtype/D.  Same arguments and semantics. */
+ * that variant does not cover dtype/D/S (see fa_variant).  Same arguments and
+ * semantics. */
 fa_status fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *lse,
                          int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale,
                          fa_dtype dtype, int variant, void *stream);

@@ -81,6 +81,11 @@ def test_unsupported_dtype_and_variant():
     assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 32, True, 0.1, fa.FA_DTYPE_BF16,
                          variant=fa.FA_VARIANT_MFMA_B128) == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16, variant=42) == fa.FA_ERR_UNSUPPORTED
+    # the ping-pong variants copy whole key tiles: S >= BK (64 or 128 keys)
+    for S, var in ((63, fa.FA_VARIANT_MFMA_B256), (1, fa.FA_VARIANT_MFMA_B256), (127, fa.FA_VARIANT_MFMA_B256_K128),
+                   (100, fa.FA_VARIANT_MFMA_B256_K128)):
+        assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, S, 128, True, 0.1, fa.FA_DTYPE_BF16,
+                             variant=var) == fa.FA_ERR_UNSUPPORTED, (S, var)
 
 
 def test_size_limits_rejected():
@@ -95,6 +100,9 @@ def test_variant_selection():
     assert fa.select_variant(1, 32, 1792, 128, bf16) == fa.FA_VARIANT_MFMA_B128
     assert fa.select_variant(1, 16, 1792, 128, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(1, 32, 2048, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
+    # below one whole 128-key tile the ping-pong kernel is not chosen
+    assert fa.select_variant(4, 80, 100, 128, bf16) == fa.FA_VARIANT_MFMA_B128
+    assert fa.select_variant(4, 80, 128, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     assert fa.select_variant(1, 1, 64, 16, f32) == fa.FA_VARIANT_VALU
     assert fa.select_variant(1, 1, 64, 16, bf16) == fa.FA_VARIANT_VALU
     assert fa.select_variant(1, 1, 64, 128, f32) == fa.FA_VARIANT_VALU

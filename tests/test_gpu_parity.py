@@ -32,6 +32,9 @@ pytestmark = pytest.mark.gpu
 # 128-query four-wave kernel, and the short-sequence kernel (pairs of 64-row
 # blocks, two key streams merged on chip)
 MFMA = ["mfma_b256", "mfma_b256_k128", "mfma_b128", "split"]
+# the ping-pong kernels copy whole key tiles (a last tile cut short is copied as
+# the sequence's last BK rows), so they take S >= BK
+PINGPONG_MIN_S = {"mfma_b256": 64, "mfma_b256_k128": 128}
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -80,6 +83,8 @@ def test_b1_h32_s1024_d128(variant, causal):
 @pytest.mark.parametrize("variant", [*MFMA, "valu"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_ragged_lengths_bf16(S, variant, D):
+    if S < PINGPONG_MIN_S.get(variant, 1):
+        pytest.skip(f"{variant} takes whole key tiles: S >= {PINGPONG_MIN_S[variant]} (FA_ERR_UNSUPPORTED below)")
     case(f"bf16 2x3x{S}x{D} causal variant={variant}")
     q, k, v = device_inputs(2, 3, S, D, seed=S)
     for causal in (True, False):
@@ -261,7 +266,8 @@ def test_resident_grid_sequences(B, H, S):
 
 
 @pytest.mark.parametrize("B,H,S,D,causal,scale", [
-    (4, 80, 100, 128, True, None),     # one-tile items: a K copy runs two items ahead
+    (4, 80, 128, 128, True, None),     # one-tile items: a K copy runs two items ahead
+    (4, 80, 200, 128, True, None),     # two-tile items, the second cut short (copied as keys 72..199)
     (4, 80, 129, 64, True, None),      # two-tile items, the second one key wide
     (1, 10, 8000, 128, False, None),   # non-causal: every item sees all 63 tiles
     (1, 5, 16384, 128, True, -0.05),   # negative scale across item boundaries

@@ -1,11 +1,14 @@
 """Guard for the inline-assembly global->LDS copies of the ping-pong kernel.
 
 The copies set M0 (the LDS destination) right before each
-global_load_lds_dwordx4 from inline assembly.  That is only sound while no
+global_load_lds_dwordx4, or before a pair of them that differ only in the
+immediate offset (-4096, then 0: the offset moves the global and the LDS
+address alike), from inline assembly.  That is only sound while no
 compiler-generated instruction in the kernel uses M0.  This test compiles the
 library to gfx950 assembly (no GPU needed) and checks, in every kernel that
-issues such copies, that each write of M0 is immediately followed by the copy
-and that no other instruction that reads M0 implicitly appears.
+issues such copies, that each write of M0 is immediately followed by a copy or
+such a pair, that every copy follows its M0 write that way, and that no other
+instruction that reads M0 implicitly appears.
 """
 import os
 import re
@@ -18,6 +21,9 @@ from tiled_online_softmax_causal_amd import build as fa_build
 # instructions that read M0 implicitly on gfx9 (besides the LDS copies themselves)
 M0_READERS = re.compile(r"\b(s_sendmsg|s_movrel|v_movrel|ds_gws|v_interp|s_set_gpr_idx|ds_.*_addtid|"
                         r"buffer_load_\w+\s.*\blds\b|global_load_lds_(?!dwordx4))")
+
+
+M0_WRITE = r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$"
 
 
 @pytest.fixture(scope="module")
@@ -65,10 +71,17 @@ def test_m0_is_only_the_lds_copy_destination(device_asm):
             assert not M0_READERS.search(ins), f"{name}: unexpected M0 reader: {ins}"
             if re.search(r"\bm0\b", ins):
                 # the LDS address, from whatever scalar register holds it
-                assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", ins), f"{name}: M0 written by: {ins}"
+                assert re.match(M0_WRITE, ins), f"{name}: M0 written by: {ins}"
                 assert body[k + 1].startswith("global_load_lds_dwordx4"), f"{name}: M0 write not followed by a copy"
             if ins.startswith("global_load_lds_dwordx4"):
-                assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", body[k - 1]), f"{name}: copy without its M0 write"
+                if re.match(M0_WRITE, body[k - 1]):
+                    continue
+                # the second copy of a pair: same operands, immediate 0, after the
+                # first at -4096, which follows the M0 write
+                first = body[k - 1]
+                assert first.startswith("global_load_lds_dwordx4") and first.endswith("offset:-4096") \
+                    and re.match(M0_WRITE, body[k - 2]), f"{name}: copy without its M0 write: {ins}"
+                assert first[:-len(" offset:-4096")] == ins, f"{name}: pair with different operands: {first} / {ins}"
 
 
 def test_copy_base_is_not_sign_extended(device_asm):

@@ -39,11 +39,16 @@ int64_t mfma_block_k(int variant) {
   return variant == FA_VARIANT_MFMA_B256_K128 ? 128 : fa::kBK;
 }
 
-bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
+// Whether a variant runs (D, dtype, S).  The ping-pong kernels copy whole key
+// tiles (a last tile cut short is copied as the sequence's last BK rows), so
+// they take S >= BK.
+bool variant_covers(int variant, int64_t D, fa_dtype dtype, int64_t S) {
   switch (variant) {
     case FA_VARIANT_MFMA_B256:
-    case FA_VARIANT_MFMA_B128:
     case FA_VARIANT_MFMA_B256_K128:
+      return dtype == FA_DTYPE_BF16 && (D == 64 || D == 128) &&
+             S >= (variant == FA_VARIANT_MFMA_B256_K128 ? 128 : 64);
+    case FA_VARIANT_MFMA_B128:
     case FA_VARIANT_SPLIT:
       return dtype == FA_DTYPE_BF16 && (D == 64 || D == 128);
     case FA_VARIANT_VALU:
@@ -55,17 +60,19 @@ bool variant_covers(int variant, int64_t D, fa_dtype dtype) {
 
 // Shape-only choice (for the 256 CUs of an MI355X): bf16 with D 64/128 runs
 // on the matrix cores, in 256-row workgroups (one per CU) with 128-key tiles
-// unless that leaves CUs idle (fewer 256-row items than CUs).  Then the split
+// unless that leaves CUs idle (fewer 256-row items than CUs) or S < 128 (the
+// kernel takes whole 128-key tiles).  Then the split
 // kernel runs pairs of 64-row blocks with four key streams per workgroup, as
 // long as its units (about one per 128 rows of a head) fit on the CUs at once;
 // beyond that the 128-row kernel, two workgroups per CU, balances better.
 int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
   if (dtype == FA_DTYPE_BF16 && (D == 64 || D == 128)) {
     constexpr int64_t kCUs = 256;
-    if (B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128)) >= kCUs) return FA_VARIANT_MFMA_B256_K128;
+    if (S >= 128 && B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128)) >= kCUs)
+      return FA_VARIANT_MFMA_B256_K128;
     return B * H * ceil_div(S, 2 * fa::split::kBQ) <= kCUs ? FA_VARIANT_SPLIT : FA_VARIANT_MFMA_B128;
   }
-  if (variant_covers(FA_VARIANT_VALU, D, dtype)) return FA_VARIANT_VALU;
+  if (variant_covers(FA_VARIANT_VALU, D, dtype, S)) return FA_VARIANT_VALU;
   return -1;
 }
 
@@ -329,7 +336,7 @@ fa_status validate_fwd(const void* q, const void* k, const void* v, const void* 
   // in-kernel offsets within one head are 32-bit; the grid is one dimension
   if (S * D >= (int64_t(1) << 31) || B > INT32_MAX / H) return FA_ERR_UNSUPPORTED;
   int var = *variant == FA_VARIANT_AUTO ? select_variant(B, H, S, D, dtype) : *variant;
-  if (!variant_covers(var, D, dtype)) return FA_ERR_UNSUPPORTED;
+  if (!variant_covers(var, D, dtype, S)) return FA_ERR_UNSUPPORTED;
   const int64_t bq = var == FA_VARIANT_VALU ? fa::kValuBQ : mfma_block_q(var);
   if (B * H * ceil_div(S, bq) > INT32_MAX) return FA_ERR_UNSUPPORTED;
   *variant = var;

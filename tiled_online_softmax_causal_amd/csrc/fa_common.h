@@ -98,5 +98,29 @@ __device__ __forceinline__ void copy16_to_lds(const void* base, unsigned voff, c
 #pragma clang diagnostic pop
 }
 
+// Two such copies 4096 bytes apart, from one offset register: base + voff_hi -
+// 4096 -> lds_dst_hi - 4096, then base + voff_hi -> lds_dst_hi.  The
+// instruction's immediate offset moves the global and the LDS address alike,
+// so the pair needs one M0 write and one offset register (the immediate is a
+// signed 13-bit field: -4096 fits, +4096 would not).  voff_hi >= 4096.
+__device__ __forceinline__ void copy16x2_to_lds(const void* base, unsigned voff_hi, char* lds_dst_hi) {
+  const unsigned dst = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds_dst_hi;
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  // (readfirstlane yields an int: widen through unsigned, never sign-extend)
+  const uint64_t sb = ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) << 32) |
+                      (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
+  base = (const void*)(uintptr_t)sb;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see copy16_to_lds
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:-4096\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(dst), "v"(voff_hi), "s"(base)
+      : "m0");
+#pragma clang diagnostic pop
+}
+
 }  // namespace common
 }  // namespace fa

@@ -311,9 +311,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     // ---- staging: HBM -> LDS directly (global_load_lds, 16 bytes per lane).
     // Thread gtid of the carrying group fills 16-byte slots gtid, gtid + 256, ...
     // (row-major) of its tensor's tile; the source is the logical chunk that the
-    // swizzle puts in that slot.  Rows past the end of the sequence re-read row
-    // S-1 (their scores are masked).  K tile T lives in K slot T % 3, V tile T
-    // in V slot T % 2.
+    // swizzle puts in that slot.  Every copy moves BK whole rows: a last tile cut
+    // short by the end of the sequence is copied as the sequence's last BK rows
+    // (keys S-BK .. S-1, so no row past S is read), and the keys it repeats from
+    // the tile before are masked (the launch takes S >= BK).  K tile T lives in
+    // K slot T % 3, V tile T in V slot T % 2.
     const int gtid = tid_s & (kGroupThreads - 1);
     const int gwave = wave & 3;
     const int g_row = gtid / G::kChunks;
@@ -322,11 +324,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     char* const vbuf0 = lds + G::kStagesK * G::kTileBytes;
     auto kslot = [](int T) { return (T + G::kStagesK) % G::kStagesK; };
     auto vslot = [](int T) { return (T + G::kStagesV) % G::kStagesV; };
-    // One tile copy: source tile (wave-uniform base), its rows left before the
-    // end of the sequence, and the ring slot.  A null tile means no copy.
+    // One tile copy: its first source row (wave-uniform) and the ring slot.
     struct Copy {
       const uint16_t* tile;
-      int rows;
       char* slot;
     };
     // The copy cursor walks this group's tensor along the tile sequence; past
@@ -340,7 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     const uint16_t* c_src = c_tensor + (size_t)cur.bh * S * D;
     int c_k = cur.k, c_left = cur.n_tiles, c_rows = S, c_slot = 0;
     auto next_copy = [&]() -> Copy {
-      const Copy c{c_src, c_rows, c_ring + c_slot};
+      // (c_rows < BK only for a last tile; S >= BK keeps the shifted start in the head)
+      const Copy c{c_rows >= BK ? c_src : c_src - (BK - c_rows) * D, c_ring + c_slot};
       c_slot = c_slot + G::kTileBytes == c_ring_bytes ? 0 : c_slot + G::kTileBytes;
       if (c_left > 1) {
         --c_left;
@@ -357,14 +358,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       }
       return c;
     };
-    // load step i of a copy: a 32-bit per-lane byte offset from the tile base;
-    // rows clamp to the sequence's last row (comparing whole offsets keeps the
-    // lane's chunk)
+    // Load steps 2j and 2j + 1 of a copy, issued as one pair: 16 bytes per lane
+    // from a 32-bit per-lane byte offset off the tile base.  The group's 256
+    // lanes cover 4096 bytes per step, in the source and in LDS alike, so the
+    // two steps of a pair share one offset register and one M0 value.
+    static_assert(G::kRowsPerLoad * G::kRowBytes == 4096 && kGroupThreads * 16 == 4096, "steps 4096 bytes apart");
+    static_assert(NL % 2 == 0, "copy steps go in pairs");
     const unsigned g_off = (unsigned)(g_row * G::kRowBytes + g_lch * 16);
-    auto copy_step = [&](int i, const Copy& c, unsigned off0) {
-      const unsigned lim = (unsigned)((c.rows - 1) * G::kRowBytes + g_lch * 16);
-      const unsigned voff = min(off0 + (unsigned)(i * G::kRowsPerLoad * G::kRowBytes), lim);
-      copy16_to_lds(c.tile, voff, c.slot + (i * kGroupThreads + gwave * 64) * 16);
+    auto copy_pair = [&](int j, const Copy& c, unsigned off0) {
+      const int i = 2 * j + 1;
+      copy16x2_to_lds(c.tile, off0 + (unsigned)(i * 4096), c.slot + (i * kGroupThreads + gwave * 64) * 16);
     };
 
     // per-lane read offsets within a tile.  K: row 32*kb + col, logical chunk
@@ -488,34 +491,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       // they would hold registers through the matrix phase
       unsigned off0 = g_off;
       asm volatile("" : "+v"(off0));
-      // copy modes: 0 none, 1 the tile's copy steps
+      // copy modes: 0 none, 1 the tile's copy steps (a pair after every second
+      // step's exponentials)
       auto copy_at = [&](int ks, auto mode_c) {
-        if (decltype(mode_c)::value != 0 && ks % (KS / NL) == 0) {
-          copy_step(ks / (KS / NL), cp, off0);
+        if (decltype(mode_c)::value != 0 && ks % (KS / NL) == 0 && (ks / (KS / NL)) % 2 == 1) {
+          copy_pair(ks / (KS / NL) / 2, cp, off0);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      using Clamped = std::integral_constant<int, 1>;
+      using WithCopies = std::integral_constant<int, 1>;
       if (t >= sp.n_w) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) set_p(ks, (bf16x8_t){});
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) copy_at(ks, Clamped{});
+        for (int ks = 0; ks < KS; ++ks) copy_at(ks, WithCopies{});
         return;
       }
       const int kv0 = t * BK;
+      // keys in the tile's LDS rows: kv0 .. kv0 + BK - 1, or S - BK .. S - 1 for a
+      // last tile cut short by S (those below kv0 repeat the tile before)
+      const int kv_row0 = min(kv0, S - BK);
       const int qi = q0w + col;
       // Tiles that straddle the diagonal or run past S move to the base-2 domain
       // here, so a hidden score is a plain -inf even when the scale is 0.
       bool masked = t >= sp.t_mask;
       const float c_t = masked ? 1.f : c_log2;
+      // Element (kb, r) sits in LDS row j = 32 kb + 8 (r / 4) + 4 half + r % 4,
+      // key kv_row0 + j; with kj = kv0 + j and d = kv0 - kv_row0 it is hidden
+      // when kj > qi + d (past the row's diagonal) or kj < kv0 + d (a key
+      // repeated from the tile before).
       auto apply_mask = [&]() {
+        const int d = kv0 - kv_row0;
+        const int qi_d = qi + d;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool hidden = (CAUSAL && kj > qi) || kj >= S;
+            const bool hidden = (CAUSAL && kj > qi_d) || kj < kv0 + d;
             sacc[kb][r] = hidden ? -__builtin_inff() : sacc[kb][r] * c_log2;
           }
       };
@@ -573,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       };
       // item start: O and l are zero, so no rescale
       if (t == 0) m_run = max_halves(sacc[0][0] * c_t);
-      exponentiate(Clamped{});
+      exponentiate(WithCopies{});
       if (__builtin_amdgcn_ballot_w64(!(rs <= kOverflowSum)) != 0) {
         // the two conditions again, from opaque copies of their bounds, rather
         // than kept as masks through the exponentials above (this path is rare)
@@ -605,9 +618,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     if (grp == 0) {
       const Copy k0 = next_copy(), k1 = next_copy();
 #pragma unroll
-      for (int i = 0; i < NL; ++i) copy_step(i, k0, g_off);
+      for (int j = 0; j < NL / 2; ++j) copy_pair(j, k0, g_off);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) copy_step(i, k1, g_off);
+      for (int j = 0; j < NL / 2; ++j) copy_pair(j, k1, g_off);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm<NL>());  // K_0 has landed
     } else {
       char* v_prev = vbuf0 + vslot(-1) * G::kTileBytes;
@@ -659,7 +672,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       {  // phase 0: no scores yet, only the copy of V_0
         const Copy cp = next_copy();
 #pragma unroll
-        for (int i = 0; i < NL; ++i) copy_step(i, cp, g_off);
+        for (int j = 0; j < NL / 2; ++j) copy_pair(j, cp, g_off);
       }
       phase_barrier();
       matrix_phase(0);  // phase 1
