@@ -21,11 +21,14 @@
 //    returns it transposed: within each 16-lane group, lane t receives
 //    element t%4 of the 4-element rows addressed by lanes t/4, t/4+4, t/4+8,
 //    t/4+12.
-//  * Each wave owns NSUB x 32 queries (NSUB = 2 by default) so that every K and
-//    V operand read from LDS feeds NSUB MFMAs; LDS read bandwidth (~128 B/clk
-//    per CU) would otherwise cap the matrix cores near their peak / 1.
-//  * K and V tiles are staged HBM -> registers -> LDS, double buffered, one
-//    barrier per tile.  LDS rows are XOR-swizzled in 16-byte chunks,
+//  * Each wave owns NSUB x 32 queries, so that every K and V operand read
+//    from LDS feeds NSUB MFMAs.  The library instantiates NSUB = 1 only: 128
+//    query rows per 4-wave workgroup, two workgroups per CU (this kernel is the
+//    128-row tiling; the 256-row ping-pong kernel is the hot path).
+//  * K and V tiles are staged HBM -> registers -> LDS (global loads into
+//    VGPRs, then LDS stores), double buffered, one barrier per tile; the
+//    ping-pong and short-sequence kernels copy HBM -> LDS directly instead.
+//    LDS rows are XOR-swizzled in 16-byte chunks,
 //    chunk' = chunk ^ f(row) with f(row) = 4*(row%4) + (row/4)%4, so the 16
 //    lanes of a 128-bit K read (16 consecutive rows) and the 32 lanes of a
 //    64-bit transposed V read (4 rows x 64 bytes) hit distinct banks of a
