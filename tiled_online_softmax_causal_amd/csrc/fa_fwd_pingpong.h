@@ -517,18 +517,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       bool masked = t >= sp.t_mask;
       const float c_t = masked ? 1.f : c_log2;
       // Element (kb, r) sits in LDS row j = 32 kb + 8 (r / 4) + 4 half + r % 4,
-      // key kv_row0 + j; with kj = kv0 + j and d = kv0 - kv_row0 it is hidden
-      // when kj > qi + d (past the row's diagonal) or kj < kv0 + d (a key
-      // repeated from the tile before).
+      // key kv_row0 + j.  It is visible from key kv0 (below it a last tile cut
+      // short by S repeats the tile before) up to the row's diagonal qi
+      // (causal).  With d = kv0 - kv_row0 and c = 32 kb + 8 (r / 4) + r % 4,
+      // that is 0 <= c + 4 half - d <= qi - kv0: one unsigned compare, as a
+      // negative left side wraps above any bound (qi >= kv0 in every tile a
+      // wave takes part in).
       auto apply_mask = [&]() {
-        const int d = kv0 - kv_row0;
-        const int qi_d = qi + d;
+        const int b = 4 * half - (kv0 - kv_row0);
+        const unsigned hi = CAUSAL ? (unsigned)(qi - kv0) : (unsigned)BK;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kj = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool hidden = (CAUSAL && kj > qi_d) || kj < kv0 + d;
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            const bool hidden = (unsigned)(c + b) > hi;
             sacc[kb][r] = hidden ? -__builtin_inff() : sacc[kb][r] * c_log2;
           }
       };
