@@ -434,7 +434,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
     auto finish_item = [&](const Item& it) {
       const int qi = it.qb * kBQ + wave * kQW + col;
       const float l_tot = sum_halves(l_run);
-      const float inv = 1.0f / l_tot;  // rows past S (l = 0) are not stored
+      // v_rcp_f32 (about 1 ulp) rather than a correctly rounded division: the
+      // products are rounded to bf16; rows past S (l = 0) are not stored
+      const float inv = __builtin_amdgcn_rcpf(l_tot);
       uint16_t* const orow = O + (size_t)it.bh * S * D + (size_t)min(qi, S - 1) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -448,15 +450,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
           const u32x2_t a0 = __builtin_bit_cast(u32x2_t, __builtin_convertvector(v0, bf16x4_t));
           const u32x2_t a1 = __builtin_bit_cast(u32x2_t, __builtin_convertvector(v1, bf16x4_t));
           // the lower half-wave keeps piece rg and needs its partner's a0; the
-          // upper keeps piece rg + 1 and needs its partner's a1
-          u32x2_t got;
+          // upper keeps piece rg + 1 and needs its partner's a1.  Swapping the
+          // upper lanes of a0 with the lower lanes of a1 gives both at once:
+          // afterwards a0 holds (own a0 | partner's a1) and a1 holds (partner's
+          // a0 | own a1) in the (lower | upper) half-wave, so every lane's piece
+          // is a0 then a1, with no per-lane selects.
+          u32x2_t x0, x1;
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const unsigned send = half ? a0[e] : a1[e];
-            const auto p = __builtin_amdgcn_permlane32_swap(send, send, false, false);
-            got[e] = half ? p[0] : p[1];
+            const auto p = __builtin_amdgcn_permlane32_swap(a0[e], a1[e], false, false);
+            x0[e] = p[0];
+            x1[e] = p[1];
           }
-          const u32x4_t piece = half ? (u32x4_t){got[0], got[1], a1[0], a1[1]} : (u32x4_t){a0[0], a0[1], got[0], got[1]};
+          const u32x4_t piece = {x0[0], x0[1], x1[0], x1[1]};
           if (qi < S) *reinterpret_cast<u32x4_t*>(orow + 32 * db + 8 * (rg + half)) = piece;
         }
       if (LSE && half == 0 && qi < S) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * common::kLn2;
