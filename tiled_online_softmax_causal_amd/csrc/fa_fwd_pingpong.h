@@ -438,6 +438,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
       // products are rounded to bf16; rows past S (l = 0) are not stored
       const float inv = __builtin_amdgcn_rcpf(l_tot);
       uint16_t* const orow = O + (size_t)it.bh * S * D + (size_t)min(qi, S - 1) * D;
+      // all pieces first, then the stores under one branch (rows past S store
+      // nothing): the pieces' multiply / convert / swap chains then overlap
+      u32x4_t piece[DB][2];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -462,9 +465,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_pingpong(
             x0[e] = p[0];
             x1[e] = p[1];
           }
-          const u32x4_t piece = {x0[0], x0[1], x1[0], x1[1]};
-          if (qi < S) *reinterpret_cast<u32x4_t*>(orow + 32 * db + 8 * (rg + half)) = piece;
+          piece[db][rg / 2] = (u32x4_t){x0[0], x0[1], x1[0], x1[1]};
         }
+      if (qi < S) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int rg = 0; rg < 4; rg += 2)
+            *reinterpret_cast<u32x4_t*>(orow + 32 * db + 8 * (rg + half)) = piece[db][rg / 2];
+      }
       if (LSE && half == 0 && qi < S) LSE[(size_t)it.bh * S + qi] = (m_run + __builtin_log2f(l_tot)) * common::kLn2;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
