@@ -117,15 +117,20 @@ def test_bf16_small_head_dims(D):
 
 # ---------------------------------------------------------------- scale and score-range edge cases
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("variant", [*MFMA, "valu"])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.0])
-def test_scale_values(variant, scale):
-    case(f"bf16 1x2x300x128 scale={scale} variant={variant}")
+def test_scale_values(variant, scale, causal):
+    """S = 300 is not a multiple of any key tile: the last tile is cut short.  With
+    scale 0 every visible key weighs the same, so a key counted twice (the
+    ping-pong kernels copy a cut-short tile as the sequence's last BK rows and mask
+    the keys it repeats) would show in the mean."""
+    case(f"bf16 1x2x300x128 scale={scale} causal={causal} variant={variant}")
     q, k, v = device_inputs(1, 2, 300, 128, seed=7)
-    o, lse = run_fwd(q, k, v, causal=True, scale=scale, variant=variant)
-    ref_o, ref_l = oracle_on(q, k, v, True, scale)
+    o, lse = run_fwd(q, k, v, causal=causal, scale=scale, variant=variant)
+    ref_o, ref_l = oracle_on(q, k, v, causal, scale)
     assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, torch.bfloat16,
-                 f"scale {scale} {variant}")
+                 f"scale {scale} causal={causal} {variant}")
 
 
 @pytest.mark.parametrize("variant", MFMA)
@@ -154,21 +159,24 @@ def test_increasing_scores_force_rescale():
                      f"growing {variant}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("variant", [*MFMA, "valu"])
-def test_scores_outgrow_fp32_range(variant):
+def test_scores_outgrow_fp32_range(variant, causal):
     """Scores that rise by ~1.85 (base 2) per key: within one 64-key tile they grow
     by ~118, so exponentiating against the previous tile's maximum would overflow
-    fp32.  Kernels that keep a stale maximum must detect that and rescale."""
-    case(f"bf16 1x2x700x128 scale=1 growing scores, variant={variant}")
+    fp32.  Kernels that keep a stale maximum must detect that and rescale.  Non-
+    causal, the largest scores sit in the cut-short last tile (S = 700), next to the
+    keys it repeats from the tile before, which must stay masked through the redo."""
+    case(f"bf16 1x2x700x128 scale=1 growing scores, causal={causal} variant={variant}")
     S, D = 700, 128
     q = torch.full((1, 2, S, D), 0.5, device="cuda")
     k = (torch.arange(S, device="cuda", dtype=torch.float32) * 0.02)[None, None, :, None].expand(1, 2, S, D)
     _, _, v = device_inputs(1, 2, S, D, seed=6)
     q, k = q.to(torch.bfloat16).contiguous(), k.to(torch.bfloat16).contiguous()
-    o, lse = run_fwd(q, k, v, causal=True, scale=1.0, variant=variant)
-    ref_o, ref_l = oracle_on(q, k, v, True, 1.0)
+    o, lse = run_fwd(q, k, v, causal=causal, scale=1.0, variant=variant)
+    ref_o, ref_l = oracle_on(q, k, v, causal, 1.0)
     assert_close(o.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, torch.bfloat16,
-                 f"outgrow {variant}")
+                 f"outgrow causal={causal} {variant}")
 
 
 @pytest.mark.parametrize("variant", MFMA)
