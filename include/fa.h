@@ -71,14 +71,18 @@ typedef enum fa_status {
  *              streams whose partial results are merged on chip.  AUTO picks
  *              it when the 256-row blocks number fewer than 256 and the pairs
  *              of 64-row blocks number at most 256; MFMA_B128 in between; and
- *              MFMA_B256_K128 from 256 blocks of 256 rows on (and S >= 128). */
+ *              MFMA_B256_K128 from 256 blocks of 256 rows on (and S >= 128).
+ *   MFMA_B128_K128: as MFMA_B128 with 128-key tiles; their 128 KB of LDS
+ *              leave one workgroup per CU (a point of the tiling sweep, never
+ *              chosen by AUTO). */
 typedef enum fa_variant {
   FA_VARIANT_AUTO = 0,
   FA_VARIANT_MFMA_B256 = 1,
   FA_VARIANT_MFMA_B128 = 2,
   FA_VARIANT_VALU = 3,
   FA_VARIANT_MFMA_B256_K128 = 4,
-  FA_VARIANT_SPLIT = 5
+  FA_VARIANT_SPLIT = 5,
+  FA_VARIANT_MFMA_B128_K128 = 6
 } fa_variant;
 
 /*

@@ -80,6 +80,8 @@ def test_unsupported_dtype_and_variant():
                          variant=fa.FA_VARIANT_MFMA_B256) == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 32, True, 0.1, fa.FA_DTYPE_BF16,
                          variant=fa.FA_VARIANT_MFMA_B128) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_FP32,
+                         variant=fa.FA_VARIANT_MFMA_B128_K128) == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_raw(P, P, P, P, 0, 1, 1, 64, 128, True, 0.1, fa.FA_DTYPE_BF16, variant=42) == fa.FA_ERR_UNSUPPORTED
     # the ping-pong variants copy whole key tiles: S >= BK (64 or 128 keys)
     for S, var in ((63, fa.FA_VARIANT_MFMA_B256), (1, fa.FA_VARIANT_MFMA_B256), (127, fa.FA_VARIANT_MFMA_B256_K128),
@@ -115,7 +117,8 @@ def test_variant_selection():
 def test_scheduler_tile_counts(S, causal):
     """The library's per-head tile count equals the causal block rule's closed form."""
     for variant, bq, bk in ((fa.FA_VARIANT_MFMA_B256, 256, 64), (fa.FA_VARIANT_MFMA_B256_K128, 256, 128),
-                            (fa.FA_VARIANT_MFMA_B128, 128, 64), (fa.FA_VARIANT_SPLIT, 64, 128),
+                            (fa.FA_VARIANT_MFMA_B128, 128, 64), (fa.FA_VARIANT_MFMA_B128_K128, 128, 128),
+                            (fa.FA_VARIANT_SPLIT, 64, 128),
                             (fa.FA_VARIANT_VALU, 64, 32)):
         assert fa.tiles_per_head(S, causal, variant) == causal_kv_tiles(S, bq, bk, causal)
     assert fa.tiles_per_head(S, causal, 0) == 0

@@ -29,9 +29,9 @@ from workloads import page_qkv, sample_rows
 pytestmark = pytest.mark.gpu
 
 # the matrix-core kernels: 256-query ping-pong with 64- and 128-key tiles, the
-# 128-query four-wave kernel, and the short-sequence kernel (pairs of 64-row
-# blocks, two key streams merged on chip)
-MFMA = ["mfma_b256", "mfma_b256_k128", "mfma_b128", "split"]
+# 128-query four-wave kernel with 64- and 128-key tiles, and the short-sequence
+# kernel (pairs of 64-row blocks, four key streams merged on chip)
+MFMA = ["mfma_b256", "mfma_b256_k128", "mfma_b128", "mfma_b128_k128", "split"]
 # the ping-pong kernels copy whole key tiles (a last tile cut short is copied as
 # the sequence's last BK rows), so they take S >= BK
 PINGPONG_MIN_S = {"mfma_b256": 64, "mfma_b256_k128": 128}
@@ -333,7 +333,7 @@ def test_deterministic_and_stream_independent():
     assert torch.equal(o0, o2) and torch.equal(l0, l2)
 
 
-@pytest.mark.parametrize("other", ["mfma_b128", "mfma_b256_k128", "split"])
+@pytest.mark.parametrize("other", ["mfma_b128", "mfma_b128_k128", "mfma_b256_k128", "split"])
 def test_variants_agree(other):
     """Different tilings and schedules give the same result within rounding."""
     case(f"bf16 2x4x777x128 mfma_b256 vs {other}")

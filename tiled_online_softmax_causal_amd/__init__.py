@@ -19,8 +19,9 @@ LIBRARY_PATH = os.path.join(_PKG, "libfa_mi355x.so")
 FA_DTYPE_FP32, FA_DTYPE_BF16 = 0, 1
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 (FA_VARIANT_AUTO, FA_VARIANT_MFMA_B256, FA_VARIANT_MFMA_B128, FA_VARIANT_VALU, FA_VARIANT_MFMA_B256_K128,
- FA_VARIANT_SPLIT) = 0, 1, 2, 3, 4, 5
-VARIANTS = {"auto": 0, "mfma_b256": 1, "mfma_b128": 2, "valu": 3, "mfma_b256_k128": 4, "split": 5}
+ FA_VARIANT_SPLIT, FA_VARIANT_MFMA_B128_K128) = 0, 1, 2, 3, 4, 5, 6
+VARIANTS = {"auto": 0, "mfma_b256": 1, "mfma_b128": 2, "valu": 3, "mfma_b256_k128": 4, "split": 5,
+            "mfma_b128_k128": 6}
 
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_ws", "fa_fwd_workspace_bytes", "fa_fwd_noalloc", "fa_fwd_variant", "fa_fwd_select_variant",
@@ -104,7 +105,9 @@ def kernel_name(variant: int, D: int, causal: bool, balanced: bool = False) -> s
     if variant == FA_VARIANT_MFMA_B256_K128:
         return f"fa::pp::attn_fwd_pingpong<{D}, 128, {c}, {bal}>"
     if variant == FA_VARIANT_MFMA_B128:
-        return f"fa::attn_fwd_mfma_bf16<{D}, 1, {c}>"
+        return f"fa::attn_fwd_mfma_bf16<{D}, 1, {c}, 64>"
+    if variant == FA_VARIANT_MFMA_B128_K128:
+        return f"fa::attn_fwd_mfma_bf16<{D}, 1, {c}, 128>"
     if variant == FA_VARIANT_SPLIT:
         return f"fa::split::attn_fwd_split<{D}, {c}>"
     if variant == FA_VARIANT_VALU:

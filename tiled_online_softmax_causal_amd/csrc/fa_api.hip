@@ -36,7 +36,7 @@ int64_t mfma_block_q(int variant) {
 
 int64_t mfma_block_k(int variant) {
   if (variant == FA_VARIANT_SPLIT) return fa::split::kBK;
-  return variant == FA_VARIANT_MFMA_B256_K128 ? 128 : fa::kBK;
+  return variant == FA_VARIANT_MFMA_B256_K128 || variant == FA_VARIANT_MFMA_B128_K128 ? 128 : fa::kBK;
 }
 
 // Whether a variant runs (D, dtype, S).  The ping-pong kernels copy whole key
@@ -49,6 +49,7 @@ bool variant_covers(int variant, int64_t D, fa_dtype dtype, int64_t S) {
       return dtype == FA_DTYPE_BF16 && (D == 64 || D == 128) &&
              S >= (variant == FA_VARIANT_MFMA_B256_K128 ? 128 : 64);
     case FA_VARIANT_MFMA_B128:
+    case FA_VARIANT_MFMA_B128_K128:
     case FA_VARIANT_SPLIT:
       return dtype == FA_DTYPE_BF16 && (D == 64 || D == 128);
     case FA_VARIANT_VALU:
@@ -76,7 +77,7 @@ int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
   return -1;
 }
 
-template <int D, int NSUB>
+template <int D, int NSUB, int BK = fa::kBK>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
                        int64_t S, int causal, float scale, hipStream_t stream) {
   const int64_t bq = 4 * 32 * NSUB;
@@ -90,10 +91,10 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* o, flo
   const auto* V = static_cast<const uint16_t*>(v);
   auto* O = static_cast<uint16_t*>(o);
   if (causal)
-    hipLaunchKernelGGL((fa::attn_fwd_mfma_bf16<D, NSUB, true>), dim3((unsigned)grid), dim3(fa::kThreads), 0,
+    hipLaunchKernelGGL((fa::attn_fwd_mfma_bf16<D, NSUB, true, BK>), dim3((unsigned)grid), dim3(fa::kThreads), 0,
                        stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)BH, c, negate_q, xcd_group);
   else
-    hipLaunchKernelGGL((fa::attn_fwd_mfma_bf16<D, NSUB, false>), dim3((unsigned)grid), dim3(fa::kThreads), 0,
+    hipLaunchKernelGGL((fa::attn_fwd_mfma_bf16<D, NSUB, false, BK>), dim3((unsigned)grid), dim3(fa::kThreads), 0,
                        stream, Q, K, V, O, lse, (int)S, (int)n_qb, (int)BH, c, negate_q, xcd_group);
   return hipGetLastError();
 }
@@ -300,7 +301,7 @@ int fa_fwd_select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype d
 int64_t fa_fwd_tiles_per_head(int64_t S, int causal, int variant) {
   int64_t bq, bk;
   if (variant == FA_VARIANT_MFMA_B256 || variant == FA_VARIANT_MFMA_B128 ||
-      variant == FA_VARIANT_MFMA_B256_K128 || variant == FA_VARIANT_SPLIT) {
+      variant == FA_VARIANT_MFMA_B256_K128 || variant == FA_VARIANT_SPLIT || variant == FA_VARIANT_MFMA_B128_K128) {
     bq = mfma_block_q(variant);
     bk = mfma_block_k(variant);
   } else if (variant == FA_VARIANT_VALU) {
@@ -364,6 +365,9 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   } else if (variant == FA_VARIANT_MFMA_B256) {
     err = D == 128 ? launch_pingpong<128, 64>(q, k, v, o, lse, BH, S, causal, scale, sched, st)
                    : launch_pingpong<64, 64>(q, k, v, o, lse, BH, S, causal, scale, sched, st);
+  } else if (variant == FA_VARIANT_MFMA_B128_K128) {
+    err = D == 128 ? launch_mfma<128, 1, 128>(q, k, v, o, lse, BH, S, causal, scale, st)
+                   : launch_mfma<64, 1, 128>(q, k, v, o, lse, BH, S, causal, scale, st);
   } else {
     err = D == 128 ? launch_mfma<128, 1>(q, k, v, o, lse, BH, S, causal, scale, st)
                    : launch_mfma<64, 1>(q, k, v, o, lse, BH, S, causal, scale, st);

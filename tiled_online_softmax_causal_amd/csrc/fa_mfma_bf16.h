@@ -61,17 +61,17 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBK = 64;  // keys per tile
 constexpr float kLn2 = 0.693147180559945309f;
 
-// Geometry of one K or V tile in LDS for head dim D (bf16).
-template <int D>
+// Geometry of one K or V tile of BK keys in LDS for head dim D (bf16).
+template <int D, int BK = kBK>
 struct TileGeo {
   static_assert(D == 64 || D == 128, "matrix-core path covers D = 64 and 128");
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row (8 or 16)
-  static constexpr int kTileBytes = kBK * kRowBytes;
+  static constexpr int kTileBytes = BK * kRowBytes;
   static constexpr int kStageBytes = 2 * kTileBytes;  // K tile then V tile
   static constexpr int kLdsBytes = 2 * kStageBytes;   // two stages
-  static constexpr int kLoadsPerThread = kBK * kChunks / kThreads;  // per tensor
-  static_assert(kBK * kChunks % kThreads == 0, "tile must split evenly over the workgroup");
+  static constexpr int kLoadsPerThread = BK * kChunks / kThreads;  // per tensor
+  static_assert(BK * kChunks % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
 // XOR key of a row's 16-byte chunks, masked to the row's chunk count.
@@ -118,9 +118,9 @@ __device__ __forceinline__ BlockCoord schedule_block(int wg, int n_qb, int BH, i
   return c;
 }
 
-template <int D>
+template <int D, int BK = kBK>
 struct TileStager {
-  static constexpr int L = TileGeo<D>::kLoadsPerThread;
+  static constexpr int L = TileGeo<D, BK>::kLoadsPerThread;
   u32x4_t kr[L], vr[L];
 
   // HBM -> registers.  Thread tid owns LDS chunks tid, tid+256, ... (row-major
@@ -145,23 +145,25 @@ struct TileStager {
     for (int i = 0; i < L; ++i) {
       const int cidx = i * kThreads + tid;
       *reinterpret_cast<u32x4_t*>(stage + cidx * 16) = kr[i];
-      *reinterpret_cast<u32x4_t*>(stage + TileGeo<D>::kTileBytes + cidx * 16) = vr[i];
+      *reinterpret_cast<u32x4_t*>(stage + TileGeo<D, BK>::kTileBytes + cidx * 16) = vr[i];
     }
   }
 };
 
-template <int D, int NSUB, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (NSUB == 1 ? 2 : 1)) void attn_fwd_mfma_bf16(
+// BK: keys per tile.  64-key tiles fit two workgroups per CU (two waves per
+// SIMD); 128-key tiles take 128 KB of LDS, so one.
+template <int D, int NSUB, bool CAUSAL, int BK = kBK>
+__global__ __launch_bounds__(kThreads, (NSUB == 1 && BK == 64 ? 2 : 1)) void attn_fwd_mfma_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int S, int n_qb, int BH, float c_log2,
     int negate_q, int xcd_group) {
-  using G = TileGeo<D>;
+  using G = TileGeo<D, BK>;
   constexpr int QW = 32 * NSUB;      // queries per wave
   constexpr int BQ = QW * kWaves;    // queries per workgroup
   constexpr int DS = D / 16;         // k-steps of the score MFMA
   constexpr int DB = D / 32;         // 32-row blocks of O^T
-  constexpr int KB = kBK / 32;       // 32-key blocks of S^T
-  constexpr int KS = kBK / 16;       // k-steps of the PV MFMA
+  constexpr int KB = BK / 32;       // 32-key blocks of S^T
+  constexpr int KS = BK / 16;       // k-steps of the PV MFMA
 
   __shared__ __attribute__((aligned(16))) char lds[G::kLdsBytes];
 
@@ -203,17 +205,17 @@ __global__ __launch_bounds__(kThreads, (NSUB == 1 ? 2 : 1)) void attn_fwd_mfma_b
   }
 
   const int kv_end = CAUSAL ? min(S, q0 + BQ) : S;
-  const int n_tiles = (kv_end + kBK - 1) / kBK;
+  const int n_tiles = (kv_end + BK - 1) / BK;
 
-  TileStager<D> stager;
+  TileStager<D, BK> stager;
   stager.load(Kh, Vh, 0, S, tid);
   stager.store(lds, tid);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = t * kBK;
+    const int kv0 = t * BK;
     const bool has_next = t + 1 < n_tiles;
-    if (has_next) stager.load(Kh, Vh, kv0 + kBK, S, tid);
+    if (has_next) stager.load(Kh, Vh, kv0 + BK, S, tid);
 
     const char* Kl = lds + (t & 1) * G::kStageBytes;
     const char* Vl = Kl + G::kTileBytes;
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(kThreads, (NSUB == 1 ? 2 : 1)) void attn_fwd_mfma_b
       // ---- mask: only tiles that straddle the diagonal or run past S.  These
       // tiles are moved to the base-2 domain here (c_t = 1 afterwards), so a
       // hidden score is a plain -inf even when the scale is 0.
-      const bool need_mask = (CAUSAL && kv0 + kBK - 1 > q0w) || (kv0 + kBK > S);
+      const bool need_mask = (CAUSAL && kv0 + BK - 1 > q0w) || (kv0 + BK > S);
       float c_t = c_log2;
       if (need_mask) {
         c_t = 1.f;
