@@ -23,11 +23,16 @@
 // double-buffered: the copies of step i+1 (HBM -> LDS directly,
 // global_load_lds) are issued between the score MFMAs of step i, every LDS
 // operand is read a few MFMAs ahead of its use (a pinned issue order), and one
-// barrier closes each step.  At the end of a block the four streams merge
-// their partial results in two rounds of pairwise exchange through LDS (the
-// stage just consumed, and the maxima and sums in a small area of their own);
-// each stream then finishes a quarter of the head dimension.  Non-causal units
-// are single blocks (all blocks weigh the same).
+// barrier closes each step.  A block's 64 Q rows are copied once into LDS
+// (the four streams share them) and each wave reads its operand from there;
+// the second block's rows replace the first's during the first block's second
+// step.  The first block's partial results stay in registers while the second
+// block's steps run; at the end of the unit the four streams merge the partial
+// results of both blocks in two rounds of pairwise exchange through LDS (one
+// stage per block, and the maxima and sums in a small area of their own),
+// sharing the rounds' barriers; each stream then finishes a quarter of the
+// head dimension.  Non-causal units are single blocks (all blocks weigh the
+// same).
 //
 // Register layout as in the other matrix-core kernels: S^T = K Q^T on
 // v_mfma_f32_32x32x16_bf16, so a lane owns one query (column lane % 32) and the
@@ -65,15 +70,18 @@ struct Geo {
   static constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row
   static constexpr int kTileBytes = kBK * kRowBytes;         // one K or V tile
   static constexpr int kStageBytes = 2 * kTileBytes;         // K then V
-  static constexpr int kMLBytes = kWaves * 2 * 64 * 4;       // the exchange's maxima and sums
-  static constexpr int kLdsBytes = 2 * kStageBytes + kMLBytes;
+  static constexpr int kMLBytes = kWaves * 2 * 64 * 4;       // the exchange's maxima and sums (one block)
+  static constexpr int kQBytes = kBQ * kRowBytes;             // one block's Q rows
+  static constexpr int kLdsBytes = 2 * kStageBytes + 2 * kMLBytes + kQBytes;
   static constexpr int kLoads = kStageBytes / (kThreads * 16);  // 16-byte copies per thread per step
+  static constexpr int kQLoads = kQBytes / (kThreads * 16);     // 16-byte copies per thread per Q block
   static constexpr int kRowsPerLoad = kThreads / kChunks;       // tile rows one copy step covers
   // the first exchange round moves half of O^T per wave (16 values per lane and
   // 32-row block of D, D/64 blocks); it must fit one stage
   static_assert(kWaves * (D / 64) * 16 * 64 * 4 <= kStageBytes, "the exchange fits one stage");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   static_assert(kLoads * kThreads * 16 == kStageBytes, "a stage splits evenly over the workgroup");
+  static_assert(kQLoads * kThreads * 16 == kQBytes, "a Q block splits evenly over the workgroup");
 };
 
 // Work unit u of a head -> its one or two query blocks (64 rows each).
@@ -130,25 +138,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
   const int n_steps = sA + (qb2 >= 0 ? (kv_end_of(qb2) + kBK - 1) / kBK : 0);
   const size_t head = (size_t)bh * S * D;
 
-  // ---- Q^T operands of both blocks: lane holds q[row][16 ds + 8 half + 0..7]
-  struct QOp {
-    bf16x8_t r[DS];
-  };
-  auto load_q = [&](int q) {
-    QOp op;
-    const int row = min(q * kBQ + 32 * rh + col, S - 1);
-    const uint16_t* src = Q + head + (size_t)row * D + 8 * half;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + 16 * ds);
-      if (negate_q) x ^= (u32x4_t){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-      op.r[ds] = __builtin_bit_cast(bf16x8_t, x);
-    }
-    return op;
-  };
-  const QOp q_a = load_q(qa);
-  const QOp q_b = load_q(qb2 >= 0 ? qb2 : qa);
-
   // ---- copies: all 512 threads fill a stage (K tile, then V tile).  Thread
   // tid writes 16-byte chunk slots tid, tid + 512, ... (row-major over the
   // swizzled tiles); its source is the logical chunk the swizzle puts in each
@@ -157,6 +146,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
   const int tid = wave * 64 + lane;
   const int c_row0 = tid / G::kChunks, c_pch = tid % G::kChunks;
   auto stage_ptr = [&](int g) { return lds + (g & 1) * G::kStageBytes; };
+  char* const q_lds = lds + 2 * G::kStageBytes + 2 * G::kMLBytes;
   // copy j of a tile (K for j < NL/2, else V) into stage dst
   auto copy_step = [&](int j, const uint16_t* kt_src, const uint16_t* vt_src, int rows, char* dst) {
     constexpr int PER = NL / 2;  // copies per tensor
@@ -165,6 +155,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
     const int lrow = min(row, rows - 1);  // the chunk keeps its swizzle column
     const unsigned off = (unsigned)(lrow * G::kRowBytes + ((c_pch ^ swz<G::kChunks>(row)) << 4));
     copy16_to_lds(x == 0 ? kt_src : vt_src, off, dst + x * G::kTileBytes + (jj * kThreads + 64 * wave) * 16);
+  };
+
+  // ---- Q of block q: the workgroup copies its 64 rows once into LDS (the
+  // layout of a K tile: swizzled 16-byte chunks; rows past the end of the
+  // sequence re-read row S-1, never stored); each wave then reads its Q^T
+  // operand, lane holding q[row][16 ds + 8 half + 0..7]
+  struct QOp {
+    bf16x8_t r[DS];
+  };
+  auto copy_q = [&](int q) {
+    const uint16_t* src = Q + head;
+#pragma unroll
+    for (int j = 0; j < G::kQLoads; ++j) {
+      const int row = j * G::kRowsPerLoad + c_row0;
+      const int grow = min(q * kBQ + row, S - 1);
+      const unsigned off = (unsigned)(grow * G::kRowBytes + ((c_pch ^ swz<G::kChunks>(row)) << 4));
+      copy16_to_lds(src, off, q_lds + (j * kThreads + 64 * wave) * 16);
+    }
+  };
+  auto read_q = [&]() {
+    QOp op;
+    const int sq = swz<G::kChunks>(col);
+    const char* base = q_lds + (32 * rh + col) * G::kRowBytes;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(base + (((2 * ds + half) ^ sq) << 4));
+      if (negate_q) x ^= (u32x4_t){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      op.r[ds] = __builtin_bit_cast(bf16x8_t, x);
+    }
+    return op;
   };
 
   // ---- LDS read offsets.  K (A operand of S^T): row 32 st + col, logical
@@ -299,19 +319,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
     }
   };
 
-  // ---- the end of a block: the four streams' partial results merge in two
-  // rounds of pairwise exchange through stage g (consumed: every wave has
-  // passed the barrier after its last read) and the maxima/sums area.  Round
-  // 1 pairs streams st and st^1; each keeps half of the 32-row blocks of O^T
-  // (st even: the lower half) and sends the other half.  Round 2 pairs st and
-  // st^2, which kept the same half; each keeps one block (the lower if st < 2)
-  // and finishes it: merges, normalises, stores (at d = 64, one block per
-  // half: streams 0 and 1 finish it, 2 and 3 only send).  The stream is a
-  // compile-time index (ST) so that the accumulator blocks are addressed
-  // statically and stay in registers.
-  float* const xb_ml = reinterpret_cast<float*>(lds + 2 * G::kStageBytes);  // [wave][m, l][lane]
-  auto finish_block_st = [&](auto st_c, int q, int g) __attribute__((always_inline)) {
+  // ---- the end of the unit: the four streams' partial results of each of
+  // its NB blocks merge in two rounds of pairwise exchange through LDS (block
+  // b through stage b, all copies landed and consumed by then, and its own
+  // maxima/sums area), the rounds of both blocks sharing their barriers.
+  // Round 1 pairs streams st and st^1; each keeps half of the 32-row blocks of
+  // O^T (st even: the lower half) and sends the other half.  Round 2 pairs st
+  // and st^2, which kept the same half; each keeps one block (the lower if
+  // st < 2) and finishes it: merges, normalises, stores (at d = 64, one block
+  // per half: streams 0 and 1 finish it, 2 and 3 only send).  The stream and
+  // the block are compile-time indices so that the accumulators are addressed
+  // statically and stay in registers.  The first block's partial results wait
+  // in registers (acc_a) while the second block's steps run.
+  struct Partial {
+    f32x16_t o[DB];
+    float m, l;
+  };
+  Partial acc_a;
+  auto finish_st = [&](auto st_c, auto nb_c, int q0, int q1) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
+    constexpr int NB = decltype(nb_c)::value;
     constexpr int H = DB / 2;                  // blocks kept after round 1
     constexpr int KEEP1 = (ST & 1) * H;        // first block kept after round 1
     constexpr int SEND1 = ((ST & 1) ^ 1) * H;  // first block sent in round 1
@@ -320,57 +347,82 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
     constexpr int SEND2 = H / 2 > 0 ? KEEP1 + ((ST >> 1) ^ 1) * H2 : KEEP1;
     constexpr bool FINISHES = H / 2 > 0 || (ST >> 1) == 0;
     constexpr int P1 = ST ^ 1, P2 = ST ^ 2;
-    float* const xb = reinterpret_cast<float*>(lds + (g & 1) * G::kStageBytes);
+    // block b's accumulator, maximum and sum: the saved first block when there
+    // are two, else the running ones
+    auto o_of = [&](auto b_c) __attribute__((always_inline)) -> f32x16_t* {
+      if constexpr (NB == 2 && decltype(b_c)::value == 0) return acc_a.o; else return oacc;
+    };
+    auto m_of = [&](auto b_c) __attribute__((always_inline)) -> float& {
+      if constexpr (NB == 2 && decltype(b_c)::value == 0) return acc_a.m; else return m_run;
+    };
+    auto l_of = [&](auto b_c) __attribute__((always_inline)) -> float& {
+      if constexpr (NB == 2 && decltype(b_c)::value == 0) return acc_a.l; else return l_run;
+    };
+    auto each_block = [&](auto&& f) __attribute__((always_inline)) {
+      f(std::integral_constant<int, 0>{});
+      if constexpr (NB == 2) f(std::integral_constant<int, 1>{});
+    };
+    auto xb_of = [&](auto b_c) { return reinterpret_cast<float*>(lds + decltype(b_c)::value * G::kStageBytes); };
+    auto ml_of = [&](auto b_c) {
+      return reinterpret_cast<float*>(lds + 2 * G::kStageBytes + decltype(b_c)::value * G::kMLBytes);
+    };
     // round 1: send half of O^T and (m, l) to stream P1
-    {
-      float* mine = xb + (size_t)wave * H * 16 * 64;
+    each_block([&](auto b_c) __attribute__((always_inline)) {
+      float* mine = xb_of(b_c) + (size_t)wave * H * 16 * 64;
+      f32x16_t* o = o_of(b_c);
 #pragma unroll
       for (int h = 0; h < H; ++h)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mine[(16 * h + r) * 64 + lane] = oacc[SEND1 + h][r];
-      xb_ml[(wave * 2 + 0) * 64 + lane] = m_run;
-      xb_ml[(wave * 2 + 1) * 64 + lane] = l_run;
-    }
+        for (int r = 0; r < 16; ++r) mine[(16 * h + r) * 64 + lane] = o[SEND1 + h][r];
+      ml_of(b_c)[(wave * 2 + 0) * 64 + lane] = m_of(b_c);
+      ml_of(b_c)[(wave * 2 + 1) * 64 + lane] = l_of(b_c);
+    });
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     phase_barrier();
-    {
+    each_block([&](auto b_c) __attribute__((always_inline)) {
       const int pw = 2 * P1 + rh;  // the partner wave
-      const float* theirs = xb + (size_t)pw * H * 16 * 64;
-      const float m_o = xb_ml[(pw * 2 + 0) * 64 + lane], l_o = xb_ml[(pw * 2 + 1) * 64 + lane];
-      const float m = fmaxf(m_run, m_o);
-      const float a_s = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+      const float* theirs = xb_of(b_c) + (size_t)pw * H * 16 * 64;
+      const float m_o = ml_of(b_c)[(pw * 2 + 0) * 64 + lane], l_o = ml_of(b_c)[(pw * 2 + 1) * 64 + lane];
+      float& m_s = m_of(b_c);
+      float& l_s = l_of(b_c);
+      f32x16_t* o = o_of(b_c);
+      const float m = fmaxf(m_s, m_o);
+      const float a_s = m_s == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_s - m);
       const float a_o = m_o == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_o - m);
 #pragma unroll
       for (int h = 0; h < H; ++h)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          oacc[KEEP1 + h][r] = oacc[KEEP1 + h][r] * a_s + theirs[(16 * h + r) * 64 + lane] * a_o;
-      l_run = l_run * a_s + l_o * a_o;
-      m_run = m;
-    }
+        for (int r = 0; r < 16; ++r) o[KEEP1 + h][r] = o[KEEP1 + h][r] * a_s + theirs[(16 * h + r) * 64 + lane] * a_o;
+      l_s = l_s * a_s + l_o * a_o;
+      m_s = m;
+    });
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     phase_barrier();
     // round 2: send a kept block and (m, l) to stream P2
-    {
-      float* mine = xb + (size_t)wave * H2 * 16 * 64;
+    each_block([&](auto b_c) __attribute__((always_inline)) {
+      float* mine = xb_of(b_c) + (size_t)wave * H2 * 16 * 64;
+      f32x16_t* o = o_of(b_c);
 #pragma unroll
       for (int h = 0; h < H2; ++h)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mine[(16 * h + r) * 64 + lane] = oacc[SEND2 + h][r];
-      xb_ml[(wave * 2 + 0) * 64 + lane] = m_run;
-      xb_ml[(wave * 2 + 1) * 64 + lane] = l_run;
-    }
+        for (int r = 0; r < 16; ++r) mine[(16 * h + r) * 64 + lane] = o[SEND2 + h][r];
+      ml_of(b_c)[(wave * 2 + 0) * 64 + lane] = m_of(b_c);
+      ml_of(b_c)[(wave * 2 + 1) * 64 + lane] = l_of(b_c);
+    });
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     phase_barrier();
-    {
+    each_block([&](auto b_c) __attribute__((always_inline)) {
       const int pw = 2 * P2 + rh;
-      const float* theirs = xb + (size_t)pw * H2 * 16 * 64;
-      const float m_o = xb_ml[(pw * 2 + 0) * 64 + lane], l_o = xb_ml[(pw * 2 + 1) * 64 + lane];
-      const float m = fmaxf(m_run, m_o);  // finite: every row sees a key in some stream
-      const float a_s = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+      const float* theirs = xb_of(b_c) + (size_t)pw * H2 * 16 * 64;
+      const float m_o = ml_of(b_c)[(pw * 2 + 0) * 64 + lane], l_o = ml_of(b_c)[(pw * 2 + 1) * 64 + lane];
+      const float m_s = m_of(b_c), l_s = l_of(b_c);
+      f32x16_t* o = o_of(b_c);
+      const float m = fmaxf(m_s, m_o);  // finite: every row sees a key in some stream
+      const float a_s = m_s == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_s - m);
       const float a_o = m_o == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_o - m);
-      const float l_tot = sum_halves(a_s * l_run + a_o * l_o);
+      const float l_tot = sum_halves(a_s * l_s + a_o * l_o);
       const float inv_s = a_s / l_tot, inv_o = a_o / l_tot;
+      const int q = decltype(b_c)::value == 0 ? q0 : q1;
       const int qi = q * kBQ + 32 * rh + col;
       uint16_t* const orow = O + head + (size_t)min(qi, S - 1) * D;
       if constexpr (FINISHES) {
@@ -382,8 +434,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
             f32x4_t v0, v1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              v0[e] = oacc[KEEP2 + h][4 * rg + e] * inv_s + theirs[(16 * h + 4 * rg + e) * 64 + lane] * inv_o;
-              v1[e] = oacc[KEEP2 + h][4 * rg + 4 + e] * inv_s + theirs[(16 * h + 4 * rg + 4 + e) * 64 + lane] * inv_o;
+              v0[e] = o[KEEP2 + h][4 * rg + e] * inv_s + theirs[(16 * h + 4 * rg + e) * 64 + lane] * inv_o;
+              v1[e] = o[KEEP2 + h][4 * rg + 4 + e] * inv_s + theirs[(16 * h + 4 * rg + 4 + e) * 64 + lane] * inv_o;
             }
             // columns 32 db + 8 rg + 4 half + 0..3 (a0) and the same for rg + 1
             // (a1); lanes l and l^32 swap so that each stores a whole 16-byte piece
@@ -403,22 +455,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
         }
       }
       if (LSE && ST == 0 && half == 0 && qi < S) LSE[(size_t)bh * S + qi] = (m + __builtin_log2f(l_tot)) * common::kLn2;
-    }
-    // the exchange areas are refilled by the next step's copies and exchange
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    phase_barrier();
+    });
   };
-  auto finish_block = [&](int q, int g) __attribute__((always_inline)) {
+  auto finish = [&](auto nb_c, int q0, int q1) __attribute__((always_inline)) {
     switch (st) {
-      case 0: finish_block_st(std::integral_constant<int, 0>{}, q, g); break;
-      case 1: finish_block_st(std::integral_constant<int, 1>{}, q, g); break;
-      case 2: finish_block_st(std::integral_constant<int, 2>{}, q, g); break;
-      default: finish_block_st(std::integral_constant<int, 3>{}, q, g); break;
+      case 0: finish_st(std::integral_constant<int, 0>{}, nb_c, q0, q1); break;
+      case 1: finish_st(std::integral_constant<int, 1>{}, nb_c, q0, q1); break;
+      case 2: finish_st(std::integral_constant<int, 2>{}, nb_c, q0, q1); break;
+      default: finish_st(std::integral_constant<int, 3>{}, nb_c, q0, q1); break;
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
-    m_run = -__builtin_inff();
-    l_run = 0.f;
   };
 
   // the tile (of the head) of the unit's step g, clamped to a valid one past the end
@@ -430,19 +475,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
     rows = S - t * kBK;
   };
 
-  // ---- prologue: the tile of step 0
+  // ---- prologue: the tile of step 0 and the first block's Q
   {
     const uint16_t *kp, *vp;
     int rows;
     copy_src(0, kp, vp, rows);
 #pragma unroll
     for (int j = 0; j < NL; ++j) copy_step(j, kp, vp, rows, stage_ptr(0));
+    copy_q(qa);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
   phase_barrier();
 
   // the steps of one block (its Q operand fixed), then the block's merge
-  auto run_block = [&](const QOp& qop, int q, int g0, int g1) __attribute__((always_inline)) {
+  // The second block's Q replaces the first's in LDS once every wave has read
+  // it (after the first step's barrier); the copy completes under the waits of
+  // the next barrier, or of the one before the second block when the first
+  // block has a single step.
+  auto run_block = [&](int q, int g0, int g1) __attribute__((always_inline)) {
+    const QOp qop = read_q();
     const int kv_end = kv_end_of(q);
     for (int g = g0; g < g1; ++g) {
       const int i = g - g0;
@@ -453,11 +504,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_split(
       step(qop, q, i, g, kn, vn, rows_n, have);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
       phase_barrier();
+      if (g == 0 && qb2 >= 0) copy_q(qb2);
     }
-    finish_block(q, g1 - 1);
   };
-  run_block(q_a, qa, 0, sA);
-  if (qb2 >= 0) run_block(q_b, qb2, sA, n_steps);
+  run_block(qa, 0, sA);
+  if (qb2 >= 0) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc_a.o[db] = oacc[db];
+      oacc[db] = (f32x16_t){};
+    }
+    acc_a.m = m_run;
+    acc_a.l = l_run;
+    m_run = -__builtin_inff();
+    l_run = 0.f;
+    if (sA == 1) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+      phase_barrier();
+    }
+    run_block(qb2, sA, n_steps);
+    finish(std::integral_constant<int, 2>{}, qa, qb2);
+  } else {
+    finish(std::integral_constant<int, 1>{}, qa, qa);
+  }
 }
 
 }  // namespace split
