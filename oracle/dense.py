@@ -21,7 +21,7 @@ DTYPE_F32, DTYPE_BF16, DTYPE_F64 = 0, 1, 2
 
 
 def default_threads() -> int:
-    """Cores this process may run on, at most 16 (a GPU machine's share of its host)."""
+    """Cores this process may run on, at most 16 (one GPU's share of an 8-GPU host)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

@@ -369,7 +369,7 @@ def test_lse_optional_and_output_buffer():
 
 
 def test_invalid_calls_enqueue_nothing():
-    case("error paths on the GPU box")
+    case("error paths on the GPU")
     q, k, v = device_inputs(1, 1, 64, 128)
     o = torch.zeros_like(q)
     with pytest.raises(ValueError):
