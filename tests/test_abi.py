@@ -99,8 +99,11 @@ def test_variant_selection():
     bf16, f32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP32
     assert fa.select_variant(8, 32, 8192, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     assert fa.select_variant(1, 32, 1024, 128, bf16) == fa.FA_VARIANT_SPLIT
-    assert fa.select_variant(1, 32, 1792, 128, bf16) == fa.FA_VARIANT_MFMA_B128
+    # between the two: the 256-row kernel below 2048 keys, the split kernel from there
+    assert fa.select_variant(1, 32, 1792, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     assert fa.select_variant(1, 16, 1792, 128, bf16) == fa.FA_VARIANT_SPLIT
+    assert fa.select_variant(1, 16, 3000, 128, bf16) == fa.FA_VARIANT_SPLIT
+    assert fa.select_variant(2, 4, 7000, 128, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(1, 32, 2048, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     # below one whole 128-key tile the ping-pong kernel is not chosen
     assert fa.select_variant(4, 80, 100, 128, bf16) == fa.FA_VARIANT_MFMA_B128

@@ -1,5 +1,6 @@
 """The library's main entry point, fa_fwd(q, k, v, o, lse, B, H, S, D, causal,
-scale, dtype, stream), called through the C ABI at the five workload shapes.
+scale, dtype, stream), called through the C ABI at the five workload shapes and
+at two shapes between the short-sequence and the full-grid choices.
 
 fa_fwd runs the automatic variant on the automatic schedule.  At each shape its
 outputs must equal fa_fwd_variant(FA_VARIANT_AUTO)'s bit for bit (the same
@@ -52,6 +53,11 @@ SHAPES = [
     ("b1 h32 S4096 d128 non-causal", 1, 32, 4096, 128, False, list(range(0, 32, 3)), 48),
     ("b8 h32 S8192 d128 causal", 8, 32, 8192, 128, True, [0, 3 * 32 + 17, 5 * 32 + 4, 7 * 32 + 31], 128),
     ("b1 h32 S32768 d128 causal", 1, 32, 32768, 128, True, [0, 31], 256),
+    # between one round of split units and a full grid of 256-row items: the
+    # 256-row kernel with idle CUs below 2048 keys, the split kernel in two
+    # rounds of units from there
+    ("b1 h32 S1792 d128 causal", 1, 32, 1792, 128, True, list(range(0, 32, 5)), 96),
+    ("b1 h16 S3000 d128 causal", 1, 16, 3000, 128, True, list(range(16)), 96),
 ]
 
 
