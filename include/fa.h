@@ -71,8 +71,9 @@ typedef enum fa_status {
  *              streams whose partial results are merged on chip.  AUTO picks
  *              MFMA_B256_K128 from 256 blocks of 256 rows on (and S >= 128);
  *              below that SPLIT while the pairs of 64-row blocks number at
- *              most 256, and beyond them SPLIT from S = 2048 on,
- *              MFMA_B256_K128 for 128 <= S < 2048 and MFMA_B128 for S < 128.
+ *              most 256; beyond them SPLIT at D = 64 or from S = 2048 on,
+ *              MFMA_B256_K128 for D = 128 and 128 <= S < 2048, and MFMA_B128
+ *              for S < 128.
  *   MFMA_B128_K128: as MFMA_B128 with 128-key tiles; their 128 KB of LDS
  *              leave one workgroup per CU (a point of the tiling sweep, never
  *              chosen by AUTO). */

@@ -99,8 +99,10 @@ def test_variant_selection():
     bf16, f32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP32
     assert fa.select_variant(8, 32, 8192, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     assert fa.select_variant(1, 32, 1024, 128, bf16) == fa.FA_VARIANT_SPLIT
-    # between the two: the 256-row kernel below 2048 keys, the split kernel from there
+    # between the two: at d = 128 the 256-row kernel below 2048 keys, the split
+    # kernel from there; at d = 64 the split kernel
     assert fa.select_variant(1, 32, 1792, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
+    assert fa.select_variant(1, 32, 1792, 64, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(1, 16, 1792, 128, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(1, 16, 3000, 128, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(2, 4, 7000, 128, bf16) == fa.FA_VARIANT_SPLIT

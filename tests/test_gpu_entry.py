@@ -58,6 +58,7 @@ SHAPES = [
     # rounds of units from there
     ("b1 h32 S1792 d128 causal", 1, 32, 1792, 128, True, list(range(0, 32, 5)), 96),
     ("b1 h16 S3000 d128 causal", 1, 16, 3000, 128, True, list(range(16)), 96),
+    ("b1 h32 S1792 d64 causal", 1, 32, 1792, 64, True, list(range(0, 32, 5)), 96),
 ]
 
 

@@ -66,17 +66,18 @@ bool variant_covers(int variant, int64_t D, fa_dtype dtype, int64_t S) {
 // 64-row blocks with four key streams per workgroup while its units (about
 // one per 128 rows of a head) fit on the CUs at once.  Between the two
 // (measured at 1152 <= S <= 7000 over several head counts) the 128-row kernel
-// was the slowest of the three by 20-60%: the 256-row kernel is taken up to
-// S < 2048, the split kernel (in more than one round of units) from there;
-// the 128-row kernel only below 128 keys.
+// was the slowest of the three: at d = 128 the 256-row kernel is taken below
+// S = 2048 and the split kernel (in more than one round of units) from there,
+// at d = 64 the split kernel throughout; the 128-row kernel only below 128
+// keys.
 int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
   if (dtype == FA_DTYPE_BF16 && (D == 64 || D == 128)) {
     constexpr int64_t kCUs = 256;
     if (S >= 128 && B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128)) >= kCUs)
       return FA_VARIANT_MFMA_B256_K128;
     if (B * H * ceil_div(S, 2 * fa::split::kBQ) <= kCUs) return FA_VARIANT_SPLIT;
-    if (S >= 2048) return FA_VARIANT_SPLIT;
-    return S >= 128 ? FA_VARIANT_MFMA_B256_K128 : FA_VARIANT_MFMA_B128;
+    if (S < 128) return FA_VARIANT_MFMA_B128;
+    return D == 64 || S >= 2048 ? FA_VARIANT_SPLIT : FA_VARIANT_MFMA_B256_K128;
   }
   if (variant_covers(FA_VARIANT_VALU, D, dtype, S)) return FA_VARIANT_VALU;
   return -1;
