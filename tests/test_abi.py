@@ -103,6 +103,9 @@ def test_variant_selection():
     # kernel from there; at d = 64 the split kernel
     assert fa.select_variant(1, 32, 1792, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     assert fa.select_variant(1, 32, 1792, 64, bf16) == fa.FA_VARIANT_SPLIT
+    # at d = 64 one 256-row item per CU still goes to the split kernel
+    assert fa.select_variant(1, 32, 2048, 64, bf16) == fa.FA_VARIANT_SPLIT
+    assert fa.select_variant(1, 32, 3000, 64, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     assert fa.select_variant(1, 16, 1792, 128, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(1, 16, 3000, 128, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(2, 4, 7000, 128, bf16) == fa.FA_VARIANT_SPLIT

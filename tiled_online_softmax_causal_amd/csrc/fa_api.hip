@@ -73,8 +73,10 @@ bool variant_covers(int variant, int64_t D, fa_dtype dtype, int64_t S) {
 int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
   if (dtype == FA_DTYPE_BF16 && (D == 64 || D == 128)) {
     constexpr int64_t kCUs = 256;
-    if (S >= 128 && B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128)) >= kCUs)
-      return FA_VARIANT_MFMA_B256_K128;
+    // at d = 64 one 256-row item per CU (items == CUs) still ran 10-14% slower
+    // than the split kernel's two rounds of units; from 384 items on it ran faster
+    const int64_t items = B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128));
+    if (S >= 128 && (D == 64 ? items > kCUs : items >= kCUs)) return FA_VARIANT_MFMA_B256_K128;
     if (B * H * ceil_div(S, 2 * fa::split::kBQ) <= kCUs) return FA_VARIANT_SPLIT;
     if (S < 128) return FA_VARIANT_MFMA_B128;
     return D == 64 || S >= 2048 ? FA_VARIANT_SPLIT : FA_VARIANT_MFMA_B256_K128;
