@@ -70,7 +70,8 @@ typedef enum fa_status {
  *              under the causal rule), as two 32-row halves times four key
  *              streams whose partial results are merged on chip.  AUTO picks
  *              MFMA_B256_K128 from 256 blocks of 256 rows on (more than 256
- *              at D = 64; and S >= 128);
+ *              at D = 64; and S >= 128), except MFMA_B128 for S < 384 with
+ *              B * H <= 384;
  *              below that SPLIT while the pairs of 64-row blocks number at
  *              most 256; beyond them SPLIT at D = 64 or from S = 2048 on,
  *              MFMA_B256_K128 for D = 128 and 128 <= S < 2048, and MFMA_B128

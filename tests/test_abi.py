@@ -110,9 +110,13 @@ def test_variant_selection():
     assert fa.select_variant(1, 16, 3000, 128, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(2, 4, 7000, 128, bf16) == fa.FA_VARIANT_SPLIT
     assert fa.select_variant(1, 32, 2048, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
-    # below one whole 128-key tile the ping-pong kernel is not chosen
+    # below one whole 128-key tile the ping-pong kernel is not chosen, nor for
+    # rows shorter than 384 keys with at most 384 heads
     assert fa.select_variant(4, 80, 100, 128, bf16) == fa.FA_VARIANT_MFMA_B128
-    assert fa.select_variant(4, 80, 128, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
+    assert fa.select_variant(4, 80, 128, 128, bf16) == fa.FA_VARIANT_MFMA_B128
+    assert fa.select_variant(8, 48, 320, 64, bf16) == fa.FA_VARIANT_MFMA_B128
+    assert fa.select_variant(8, 64, 256, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
+    assert fa.select_variant(4, 80, 400, 128, bf16) == fa.FA_VARIANT_MFMA_B256_K128
     assert fa.select_variant(1, 1, 64, 16, f32) == fa.FA_VARIANT_VALU
     assert fa.select_variant(1, 1, 64, 16, bf16) == fa.FA_VARIANT_VALU
     assert fa.select_variant(1, 1, 64, 128, f32) == fa.FA_VARIANT_VALU

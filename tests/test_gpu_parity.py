@@ -240,12 +240,12 @@ def test_long_sequences_sampled(B, H, S, n_rows):
     torch.cuda.empty_cache()
 
 
-def _run_poisoned(q, k, v, causal, scale):
+def _run_poisoned(q, k, v, causal, scale, variant="auto"):
     """The forward into NaN-filled outputs; every element must come out finite (no
     work item skipped, none written twice with a stale value)."""
     o = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
-    fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse, variant=variant)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), "rows left unwritten"
     return o, lse
@@ -285,11 +285,12 @@ def test_resident_grid_edge_items(B, H, S, D, causal, scale):
     """Resident grids (more items than CUs) at the edges of the item chaining: the tile
     sequence of a workgroup runs across item boundaries, where one matrix phase
     finishes an item and starts the next.  Sampled rows of every head (all rows for
-    the short sequences)."""
+    the short sequences).  The ping-pong kernel is named explicitly: for the shortest
+    of these shapes the automatic choice is the 128-row kernel."""
     scale = scale_of(D) if scale is None else scale
     case(f"bf16 {B}x{H}x{S}x{D} causal={causal} scale={scale}, resident grid")
     q, k, v = device_inputs(B, H, S, D, seed=S + D)
-    o, lse = _run_poisoned(q, k, v, causal, scale)
+    o, lse = _run_poisoned(q, k, v, causal, scale, variant="mfma_b256_k128")
     rows = np.arange(S) if S <= 256 else sample_rows(S, 16, tile_edges=(128, 256))
     bh = list(range(B * H))
     ref_o, ref_l = oracle_on(q, k, v, causal, scale, bh_idx=bh, row_idx=rows)

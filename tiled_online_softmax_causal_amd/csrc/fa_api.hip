@@ -76,7 +76,14 @@ int select_variant(int64_t B, int64_t H, int64_t S, int64_t D, fa_dtype dtype) {
     // at d = 64 one 256-row item per CU (items == CUs) still ran 10-14% slower
     // than the split kernel's two rounds of units; from 384 items on it ran faster
     const int64_t items = B * H * ceil_div(S, mfma_block_q(FA_VARIANT_MFMA_B256_K128));
-    if (S >= 128 && (D == 64 ? items > kCUs : items >= kCUs)) return FA_VARIANT_MFMA_B256_K128;
+    if (S >= 128 && (D == 64 ? items > kCUs : items >= kCUs)) {
+      // rows shorter than 384 keys with at most 384 heads: the 128-row kernel
+      // (two workgroups per CU, no ping-pong start-up per item) ran 4-30%
+      // faster (b4 h80 and b8 h48 at S 128-320); with 512 heads at S 256 it
+      // ran 16% slower
+      if (S < 384 && B * H <= 384) return FA_VARIANT_MFMA_B128;
+      return FA_VARIANT_MFMA_B256_K128;
+    }
     if (B * H * ceil_div(S, 2 * fa::split::kBQ) <= kCUs) return FA_VARIANT_SPLIT;
     if (S < 128) return FA_VARIANT_MFMA_B128;
     return D == 64 || S >= 2048 ? FA_VARIANT_SPLIT : FA_VARIANT_MFMA_B256_K128;
