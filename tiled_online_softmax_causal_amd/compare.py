@@ -21,6 +21,13 @@ dP).  The second form turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 counter files of such a run into measured HBM bytes per call of each path,
 scaled by the counters of a plain device copy of known size
 (bench.py --copy-calibration).
+
+    python -m tiled_online_softmax_causal_amd.compare --auto-check N [--shape-seed 7]
+
+times each matrix-core tiling (mfma_b256_k128, mfma_b128, split; fa_fwd_variant)
+on N seeded random causal bf16 shapes (B in 1..8, H in 4..64, S log-uniform in
+128..16384, d 64 or 128) and prints one JSON line per shape with the tiling the
+automatic choice (fa_fwd) takes and its time over the fastest tiling's.
 """
 from __future__ import annotations
 
@@ -165,11 +172,17 @@ def main():
     ap.add_argument("--inputs", choices=("uniform", "zeros"), default="uniform",
                     help="uniform(-0.8, 0.8) (the workload) or all-zero Q, K, V: the same instructions with "
                          "no switching in the matrix-core operands, to separate power from issue limits")
+    ap.add_argument("--auto-check", type=int, default=0, metavar="N",
+                    help="time the automatic choice against each matrix-core tiling on N random shapes")
+    ap.add_argument("--shape-seed", type=int, default=7)
     ap.add_argument("--clock", metavar="GRBM_CSV",
                     help="rocprofv3 --pmc GRBM_GUI_ACTIVE counter file -> mean GPU clock of each path's kernels")
     args = ap.parse_args()
     if args.clock:
         print(json.dumps(clock(args.clock)))
+        return
+    if args.auto_check:
+        auto_check(args.auto_check, args.shape_seed)
         return
     seqs = page_grid() if args.seq == "grid48" else [int(s) for s in args.seq.split(",")]
     if args.traffic and args.per_call:
@@ -250,6 +263,66 @@ def main():
             }), flush=True)
             del ws
             torch.cuda.empty_cache()
+        del q, k, v
+        torch.cuda.empty_cache()
+
+
+def auto_check(n: int, seed: int):
+    """The automatic choice (fa_fwd) against each matrix-core tiling on n seeded random shapes."""
+    import random
+
+    import torch
+
+    import tiled_online_softmax_causal_amd as fa
+    from tiled_online_softmax_causal_amd.costmodel import attention_flops
+    from workloads import uniform_qkv_device
+
+    rng = random.Random(seed)
+    shapes = []
+    while len(shapes) < n:
+        D = rng.choice([64, 128])
+        B = rng.choice([1, 1, 2, 4, 8])
+        H = rng.choice([4, 8, 12, 16, 24, 32, 48, 64])
+        S = int(2 ** rng.uniform(math.log2(128), math.log2(16384)))
+        if B * H * S * D <= 2**29:  # at most 1 GiB per bf16 tensor
+            shapes.append((B, H, S, D))
+    tilings = ["mfma_b256_k128", "mfma_b128", "split"]
+    names = {v: k for k, v in fa.VARIANTS.items()}
+    us_all = []
+    for B, H, S, D in shapes:
+        q, k, v = uniform_qkv_device(B, H, S, D, seed=42, dtype=torch.bfloat16, device="cuda")
+        scale = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32).item())
+        flops = attention_flops(B, H, S, D, True)
+        reps = max(3, min(50, int(4e14 / (flops * 1e3 + 1))))
+        us = {}
+        order = tilings[len(us_all) % 3:] + tilings[:len(us_all) % 3]  # rotate: no tiling always first
+        for var in order:
+            # warm up for about 30 ms: under load the clock takes a few ms to settle
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                fa.fwd(q, k, v, causal=True, scale=scale, variant=var)
+            e1.record()
+            torch.cuda.synchronize()
+            per_call = max(e0.elapsed_time(e1) / 3, 1e-3)
+            for _ in range(min(200, int(30.0 / per_call))):
+                fa.fwd(q, k, v, causal=True, scale=scale, variant=var)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fa.fwd(q, k, v, causal=True, scale=scale, variant=var)
+            e1.record()
+            torch.cuda.synchronize()
+            us[var] = e0.elapsed_time(e1) / reps * 1e3
+        us_all.append(us)
+        best = min(tilings, key=us.get)
+        # fa_fwd runs exactly the chosen tiling's kernel and schedule, so the
+        # choice is judged on that tiling's own timing
+        choice = names.get(fa.select_variant(B, H, S, D), "?")
+        print(json.dumps({"shape": [B, H, S, D], "us": {k_: round(x, 1) for k_, x in us.items()},
+                          "auto_variant": choice, "fastest_tiling": best,
+                          "choice_over_fastest": round(us[choice] / us[best], 3) if choice in us else None}),
+              flush=True)
         del q, k, v
         torch.cuda.empty_cache()
 
