@@ -200,7 +200,7 @@ def main():
         record_traffic(args.workload, *args.record_traffic, args.copy_mib)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: this library has no multi-GPU path "
               "(the forward pass shards over (batch, head) with no communication; run one process per GPU)",
               file=sys.stderr)
         sys.exit(2)
